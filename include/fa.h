@@ -1,0 +1,169 @@
+/*
+ * fa.h - C ABI of libfa.so: masked scaled-dot-product attention forward on MI355X (gfx950).
+ *
+ *   O = softmax(scale * Q K^T + bias, masked) V,   plus the fp32 log-sum-exp of each row.
+ *
+ * The operation and its mask family follow the pages this library is built from:
+ * - "sparseMode介绍" (CANN aolapi common parameter page): attenMask True = masked, and
+ *   sparseMode 0..8 (sections sparseMode=0 .. sparseMode=8), including the varlen split
+ *   modes 7/8 with their cumulative actual_seq_qlen / actual_seq_kvlen arrays.
+ * - "压缩mask" (CANN ATB compressed-mask page), alibi scenario: per-head slope times a
+ *   right-aligned relative-position bias; masks aligned from kvSeqLen and qSeqLen.
+ * - "Ý Tưởng Tiling & Online Softmax Trong FlashAttention" (exercise page), knowledge goals:
+ *   block tiling with a running row maximum and running sum, never forming the Sq x Skv
+ *   matrix.
+ * - "aclnnScatterPaKvCache" (ops-transformer doc), sections "函数原型" and the return-code
+ *   table: the two-phase call (workspace size first, then execute on a stream) and
+ *   validation with status codes before any device work. The codes below are this
+ *   library's own.
+ *
+ * Conventions shared by every entry point:
+ * - Device buffers (q, k, v, out, softmax_lse, alibi_slopes, atten_mask, workspace and the
+ *   probe outputs) are allocated and owned by the caller and must be contiguous in the
+ *   stated layout. The library never allocates device memory.
+ * - actual_seq_qlen, actual_seq_kvlen and prefix are HOST int64 arrays, read during the call
+ *   only.
+ * - Every argument is validated on the host before anything is enqueued. On any error the
+ *   call returns a non-zero status and writes nothing.
+ * - Compute calls are asynchronous on `stream` (a hipStream_t, 0 = the null stream); the
+ *   caller synchronises. Results are bitwise deterministic for identical inputs (no
+ *   atomics), as the ops-transformer doc asks of its ops ("确定性计算").
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fa_status;
+#define FA_OK 0
+#define FA_ERR_NULLPTR 1        /* a required pointer is NULL                                */
+#define FA_ERR_PARAM_INVALID 2  /* a value breaks a rule of the pages or of this ABI         */
+#define FA_ERR_UNSUPPORTED 3    /* valid per the pages but not built (e.g. D > 128)          */
+#define FA_ERR_HIP 4            /* the HIP runtime reported an error (launch, copy, device)  */
+#define FA_ERR_WORKSPACE 5      /* workspace smaller than fa_fwd_workspace_size asked for    */
+
+/* Tensor layouts. BNSD: [B, N, S, D]. BSND: [B, S, N, D]. TND: [T, N, D], the B sequences
+ * packed back to back; sequence b occupies tokens [cum[b-1], cum[b]) of the cumulative
+ * arrays (cum[-1] = 0). */
+#define FA_LAYOUT_BNSD 0
+#define FA_LAYOUT_BSND 1
+#define FA_LAYOUT_TND 2
+
+/* Element types of q, k, v and out (all four share one). softmax_lse is always fp32. */
+#define FA_DTYPE_F32 0
+#define FA_DTYPE_F16 1
+#define FA_DTYPE_BF16 2
+
+/* Problem sizes. B batches, N heads (q, k and v have the same N), head size D.
+ * BNSD/BSND: every batch has Sq queries and Skv keys; T_q / T_kv are ignored.
+ * TND: Sq / Skv are ignored; T_q / T_kv are the total token counts and must equal the last
+ * entries of actual_seq_qlen / actual_seq_kvlen. */
+typedef struct fa_dims {
+    int32_t dtype;
+    int64_t B, N, Sq, Skv, D;
+    int64_t T_q, T_kv;
+} fa_dims;
+
+/* Mask arguments, shared by fa_fwd and fa_mask_probe.
+ *
+ * sparse_mode ("sparseMode介绍"):
+ *   0 defaultMask: row i sees columns j with -pre_tokens <= j - i <= next_tokens (offsets from
+ *     the top-left). pre/next >= max(Sq, Skv) (e.g. INT64_MAX) is "no mask". Negative
+ *     next_tokens needs pre_tokens >= |next_tokens| and |next_tokens| < Skv; negative
+ *     pre_tokens needs next_tokens >= |pre_tokens| and |pre_tokens| < Sq.
+ *   1 allMask: atten_mask (uint8, non-zero = masked) gives every entry; pre/next ignored.
+ *     Shape [B or 1, N or 1, Sq, Skv]: mask_bcast[0] / mask_bcast[1] non-zero means the batch
+ *     / head dimension has size 1 and is shared. BNSD/BSND only.
+ *   2 leftUpCausal: j <= i.
+ *   3 rightDownCausal: j <= i + (Skv_b - Sq_b).
+ *   4 band from the bottom-right: -pre <= j - i - (Skv_b - Sq_b) <= next, pre + next >= 0.
+ *   5, 6 prefix: rightDownCausal, plus columns j < prefix[b] for every row.
+ *   7 (TND only): the last batch with Sq_b > 0 and Skv_b > 0 uses rule 4, with
+ *     pre >= Skv_b and Sq_b - Skv_b <= next <= 0; every other batch uses rule 3 and needs
+ *     Sq_b <= Skv_b. No alibi.
+ *   8 (TND only): the first such batch uses rule 4 with pre >= Skv_b and
+ *     next >= Sq_b - Skv_b; every other batch uses rule 2. No alibi.
+ * pre_tokens / next_tokens are ignored (and not checked) in modes 1, 2, 3, 5 and 6.
+ * Rows with no visible column produce O = 0 and LSE = -inf. */
+
+/* Phase 1: validate the sizes and return the workspace size fa_fwd needs (in bytes; 0 means
+ * no workspace). Host only; never touches the GPU. */
+fa_status fa_fwd_workspace_size(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                                const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                                size_t* bytes);
+
+/* Phase 2: the forward pass.
+ *   q, k, v, out:  device, dims->dtype, in `layout`.
+ *   softmax_lse:   device fp32, [B, N, Sq] (BNSD/BSND) or [N, T_q] (TND); natural log of the
+ *                  sum over visible j of exp(scale * q_i.k_j + bias_ij).
+ *   alibi_slopes:  device fp32 [N] or NULL. When given, bias_ij = slope_h * (j - i - (Skv_b - Sq_b))
+ *                  ("压缩mask", alibi scenario, right-aligned); D <= 128; not with modes 7/8.
+ *   scale:         softmax scale, finite and > 0 (e.g. 1/sqrt(D)).
+ *   workspace:     device, at least fa_fwd_workspace_size bytes (may be NULL when that is 0).
+ * Supported: D <= 128 for every dtype; the MFMA kernels serve fp16/bf16 with D = 64 or 128,
+ * a generic kernel everything else. */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* softmax_lse,
+                 const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                 int64_t pre_tokens, int64_t next_tokens,
+                 const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                 const int64_t* prefix, const float* alibi_slopes,
+                 const uint8_t* atten_mask, const int64_t* mask_bcast,
+                 float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Mask probe: runs the same device mask code the forward kernels use, without any
+ * attention arithmetic.
+ *   row_visible_counts: device int64, laid out like softmax_lse ([B, N, Sq] or [N, T_q]):
+ *                       the number of visible columns of each row.
+ *   tile_class:         device uint8 or NULL, [n_qtiles_total, n_kvtiles_max] (see
+ *                       fa_tile_shape): 0 = the forward kernel skips the tile (never loads
+ *                       it), 1 = visited with per-element masking, 2 = visited without
+ *                       masking (every in-range entry visible), 3 = outside the sequence.
+ *                       Row r of the map is the q tile r of the batch-major enumeration
+ *                       (batch 0's tiles first). Mode 1 is not tiled (NULL required).
+ * The workspace argument has fa_fwd's meaning and size. Asynchronous on `stream`. */
+fa_status fa_mask_probe(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                        int64_t pre_tokens, int64_t next_tokens,
+                        const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                        const int64_t* prefix, const uint8_t* atten_mask,
+                        const int64_t* mask_bcast, int64_t* row_visible_counts,
+                        uint8_t* tile_class, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Tile shape the forward kernel will use for these sizes: block_m query rows by block_n
+ * keys, the number of q tiles (all batches) and the largest number of kv tiles of a batch.
+ * Host only. */
+fa_status fa_tile_shape(const fa_dims* dims, int32_t layout, const int64_t* actual_seq_qlen,
+                        const int64_t* actual_seq_kvlen, int32_t* block_m, int32_t* block_n,
+                        int64_t* n_qtiles_total, int64_t* n_kvtiles_max);
+
+/* Host-side plan summary of one fa_fwd call (same validation as fa_fwd, no device work).
+ * kernel: 0 = generic, 1 = MFMA. Tile counts are per head. */
+typedef struct fa_plan_stats {
+    int32_t kernel;
+    int32_t block_m, block_n;
+    int64_t work_items;        /* (batch, q tile) pairs, per head                       */
+    int64_t kv_tiles_visited;  /* kv tiles loaded, summed over work items, per head     */
+    int64_t kv_tiles_full;     /* of which need no per-element masking                  */
+    int64_t kv_tiles_total;    /* kv tiles a dense pass would load, per head            */
+    size_t workspace_bytes;
+} fa_plan_stats;
+
+fa_status fa_plan_stats_get(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                            int64_t pre_tokens, int64_t next_tokens,
+                            const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                            const int64_t* prefix, int32_t has_alibi, int32_t has_mask,
+                            float scale, fa_plan_stats* out);
+
+/* A static, human-readable name for a status code. */
+const char* fa_status_str(fa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

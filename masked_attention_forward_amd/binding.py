@@ -1,0 +1,248 @@
+"""ctypes binding to libfa.so (include/fa.h). Argument marshalling only.
+
+Every computation runs in the library's HIP kernels; this module turns torch tensors into raw
+pointers and sizes, passes torch's current HIP stream, and raises on a non-zero status. If
+the library is missing it raises instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+FA_LAYOUTS = {"BNSD": 0, "BSND": 1, "TND": 2}
+_DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULLPTR", 2: "FA_ERR_PARAM_INVALID",
+                3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_HIP", 5: "FA_ERR_WORKSPACE"}
+
+
+class FaDims(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("B", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("Sq", ctypes.c_int64), ("Skv", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("T_q", ctypes.c_int64), ("T_kv", ctypes.c_int64)]
+
+
+class FaPlanStats(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("work_items", ctypes.c_int64), ("kv_tiles_visited", ctypes.c_int64),
+                ("kv_tiles_full", ctypes.c_int64), ("kv_tiles_total", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({fa_status_str(status)})")
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.environ.get("FA_LIBRARY", os.path.join(HERE, "lib", "libfa.so"))
+
+
+def load_library():
+    """Load libfa.so (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfa.so is not built ({path}); run `python -m masked_attention_forward_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pdims = ctypes.POINTER(FaDims)
+    pi64 = ctypes.POINTER(ctypes.c_int64)
+    lib.fa_fwd_workspace_size.argtypes = [pdims, i32, i32, pi64, pi64, ctypes.POINTER(sz)]
+    lib.fa_fwd_workspace_size.restype = i32
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
+                           vp, vp, pi64, ctypes.c_float, vp, sz, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_mask_probe.argtypes = [pdims, i32, i32, i64, i64, pi64, pi64, pi64, vp, pi64, vp, vp,
+                                  vp, sz, vp]
+    lib.fa_mask_probe.restype = i32
+    lib.fa_tile_shape.argtypes = [pdims, i32, pi64, pi64, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                  pi64, pi64]
+    lib.fa_tile_shape.restype = i32
+    lib.fa_plan_stats_get.argtypes = [pdims, i32, i32, i64, i64, pi64, pi64, pi64, i32, i32,
+                                      ctypes.c_float, ctypes.POINTER(FaPlanStats)]
+    lib.fa_plan_stats_get.restype = i32
+    lib.fa_status_str.argtypes = [i32]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def fa_status_str(status: int) -> str:
+    return load_library().fa_status_str(int(status)).decode()
+
+
+def _i64(seq: Optional[Sequence[int]]):
+    if seq is None:
+        return None
+    vals = [int(x) for x in seq]
+    return (ctypes.c_int64 * max(len(vals), 1))(*vals)
+
+
+def _layout_code(layout) -> int:
+    if isinstance(layout, str):
+        return FA_LAYOUTS[layout]
+    return int(layout)
+
+
+def make_dims(dtype, layout, *, B=0, N=1, Sq=0, Skv=0, D=1, T_q=0, T_kv=0) -> FaDims:
+    code = _DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return FaDims(code, B, N, Sq, Skv, D, T_q, T_kv)
+
+
+def dims_of(q: torch.Tensor, k: torch.Tensor, layout, actual_seq_qlen=None) -> FaDims:
+    """fa_dims for q / k in `layout` (shapes only)."""
+    lay = _layout_code(layout)
+    if q.dtype not in _DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if lay == 0:
+        B, N, Sq, D = q.shape
+        return make_dims(q.dtype, lay, B=B, N=N, Sq=Sq, Skv=k.shape[2], D=D)
+    if lay == 1:
+        B, Sq, N, D = q.shape
+        return make_dims(q.dtype, lay, B=B, N=N, Sq=Sq, Skv=k.shape[1], D=D)
+    T_q, N, D = q.shape
+    B = len(actual_seq_qlen) if actual_seq_qlen is not None else 0
+    return make_dims(q.dtype, lay, B=B, N=N, D=D, T_q=T_q, T_kv=k.shape[0])
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_device_tensor(name, t, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def fa_fwd_workspace_size(dims: FaDims, layout, sparse_mode: int, actual_seq_qlen=None,
+                          actual_seq_kvlen=None) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    st = lib.fa_fwd_workspace_size(ctypes.byref(dims), _layout_code(layout), int(sparse_mode),
+                                   _i64(actual_seq_qlen), _i64(actual_seq_kvlen), ctypes.byref(out))
+    if st != 0:
+        raise FaError(st, "fa_fwd_workspace_size")
+    return int(out.value)
+
+
+def fa_fwd(q, k, v, out, softmax_lse, *, layout="BNSD", sparse_mode: int = 0, pre_tokens: int = 0,
+           next_tokens: int = 0, actual_seq_qlen=None, actual_seq_kvlen=None, prefix=None,
+           alibi_slopes: Optional[torch.Tensor] = None, atten_mask: Optional[torch.Tensor] = None,
+           mask_bcast=None, scale: float, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> None:
+    """Calls fa_fwd on device tensors. Raises FaError on a non-zero status."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_device_tensor(name, t, q.dtype)
+    _check_device_tensor("softmax_lse", softmax_lse, torch.float32)
+    _check_device_tensor("alibi_slopes", alibi_slopes, torch.float32)
+    if atten_mask is not None:
+        _check_device_tensor("atten_mask", atten_mask)
+        if atten_mask.dtype not in (torch.uint8, torch.bool):
+            raise TypeError("atten_mask must be uint8 or bool")
+    dims = dims_of(q, k, layout, actual_seq_qlen)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_lse), ctypes.byref(dims),
+                    _layout_code(layout), int(sparse_mode), int(pre_tokens), int(next_tokens),
+                    _i64(actual_seq_qlen), _i64(actual_seq_kvlen), _i64(prefix), _ptr(alibi_slopes),
+                    _ptr(atten_mask), _i64(mask_bcast), float(scale), _ptr(workspace), ws_bytes,
+                    stream if stream is not None else _stream(q.device))
+    if st != 0:
+        raise FaError(st, "fa_fwd")
+
+
+def lse_shape(q, layout, actual_seq_qlen=None):
+    lay = _layout_code(layout)
+    if lay == 0:
+        return (q.shape[0], q.shape[1], q.shape[2])
+    if lay == 1:
+        return (q.shape[0], q.shape[2], q.shape[1])
+    return (q.shape[1], q.shape[0])
+
+
+def flash_attention(q, k, v, *, layout="BNSD", sparse_mode: int = 0, scale: float, **kw):
+    """Allocates out / softmax_lse / workspace and runs fa_fwd. Returns (out, softmax_lse)."""
+    out = torch.empty_like(q)
+    lse = torch.empty(lse_shape(q, layout), dtype=torch.float32, device=q.device)
+    dims = dims_of(q, k, layout, kw.get("actual_seq_qlen"))
+    ws = fa_fwd_workspace_size(dims, layout, sparse_mode, kw.get("actual_seq_qlen"),
+                               kw.get("actual_seq_kvlen"))
+    workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    fa_fwd(q, k, v, out, lse, layout=layout, sparse_mode=sparse_mode, scale=scale,
+           workspace=workspace, **kw)
+    return out, lse
+
+
+def fa_tile_shape(dims: FaDims, layout, actual_seq_qlen=None, actual_seq_kvlen=None):
+    """(block_m, block_n, n_qtiles_total, n_kvtiles_max)."""
+    lib = load_library()
+    bm, bn = ctypes.c_int32(0), ctypes.c_int32(0)
+    nq, nk = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib.fa_tile_shape(ctypes.byref(dims), _layout_code(layout), _i64(actual_seq_qlen),
+                           _i64(actual_seq_kvlen), ctypes.byref(bm), ctypes.byref(bn),
+                           ctypes.byref(nq), ctypes.byref(nk))
+    if st != 0:
+        raise FaError(st, "fa_tile_shape")
+    return bm.value, bn.value, nq.value, nk.value
+
+
+def fa_plan_stats(dims: FaDims, layout, sparse_mode: int, *, pre_tokens=0, next_tokens=0,
+                  actual_seq_qlen=None, actual_seq_kvlen=None, prefix=None, has_alibi=False,
+                  has_mask=False, scale=1.0) -> dict:
+    """Host-side plan summary of a fa_fwd call (no device work)."""
+    lib = load_library()
+    s = FaPlanStats()
+    st = lib.fa_plan_stats_get(ctypes.byref(dims), _layout_code(layout), int(sparse_mode),
+                               int(pre_tokens), int(next_tokens), _i64(actual_seq_qlen),
+                               _i64(actual_seq_kvlen), _i64(prefix), int(has_alibi), int(has_mask),
+                               float(scale), ctypes.byref(s))
+    if st != 0:
+        raise FaError(st, "fa_plan_stats_get")
+    return {f: getattr(s, f) for f, _ in FaPlanStats._fields_}
+
+
+def fa_mask_probe(dims: FaDims, layout, sparse_mode: int, *, device, pre_tokens=0, next_tokens=0,
+                  actual_seq_qlen=None, actual_seq_kvlen=None, prefix=None, atten_mask=None,
+                  mask_bcast=None, tiles: bool = True):
+    """Runs fa_mask_probe; returns (row_visible_counts, tile_class or None) on `device`."""
+    lib = load_library()
+    lay = _layout_code(layout)
+    if lay == 2:
+        counts = torch.empty((dims.N, dims.T_q), dtype=torch.int64, device=device)
+    else:
+        counts = torch.empty((dims.B, dims.N, dims.Sq), dtype=torch.int64, device=device)
+    tile = None
+    if tiles and sparse_mode != 1:
+        _, _, nq, nk = fa_tile_shape(dims, layout, actual_seq_qlen, actual_seq_kvlen)
+        tile = torch.empty((nq, nk), dtype=torch.uint8, device=device)
+    ws = fa_fwd_workspace_size(dims, layout, sparse_mode, actual_seq_qlen, actual_seq_kvlen)
+    workspace = torch.empty(ws, dtype=torch.uint8, device=device) if ws else None
+    st = lib.fa_mask_probe(ctypes.byref(dims), lay, int(sparse_mode), int(pre_tokens), int(next_tokens),
+                           _i64(actual_seq_qlen), _i64(actual_seq_kvlen), _i64(prefix),
+                           _ptr(atten_mask), _i64(mask_bcast), _ptr(counts), _ptr(tile),
+                           _ptr(workspace), ws, _stream(device))
+    if st != 0:
+        raise FaError(st, "fa_mask_probe")
+    return counts, tile

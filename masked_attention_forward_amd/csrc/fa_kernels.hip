@@ -1,0 +1,697 @@
+// fa_kernels.hip - masked attention forward kernels for gfx950 (MI355X) and the device half
+// of the C ABI (fa_fwd, fa_mask_probe).
+//
+// The method is FlashAttention-style tiling with an online softmax ("Ý Tưởng Tiling & Online
+// Softmax Trong FlashAttention", knowledge goals): K/V blocks stream past a block of query
+// rows that keeps a running row maximum m and running sum l, so the Sq x Skv score matrix
+// never exists. The mask family is "sparseMode介绍" (sparseMode 0..8), turned into per-row
+// column intervals by fa_mask.h; the alibi bias is "压缩mask"'s per-head slope times a
+// right-aligned relative position.
+//
+// Two kernel families:
+//  * fa_fwd_mfma: fp16 / bf16, D in {64, 128}. A 256-thread workgroup owns 128 query rows
+//    (4 waves x 32 rows). Each kv tile is 64 keys. Per wave and tile it computes
+//    S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}, so each lane ends up holding one query
+//    row (and 32 of the tile's 64 keys); softmax statistics are lane-local plus one exchange
+//    with lane^32. Then O^T += V^T P^T with the same MFMA, P taken straight from the S^T
+//    accumulators (no data movement), V^T read from an LDS copy that was transposed on the
+//    way in. K and V tiles are double-buffered in LDS with 128-bit coalesced global loads
+//    prefetched one tile ahead; LDS layouts are XOR-swizzled so the 16-byte operand reads
+//    hit distinct banks.
+//  * fa_fwd_generic: any dtype (fp32 included), D <= 128. One thread per query row, fp32
+//    throughout (P is never rounded), K/V tiles of 16 keys staged in LDS.
+// Both visit only kv tiles that hold a visible entry (fa_tile_kv_range) and skip
+// per-element masking on tiles that are fully visible (fa_tile_full).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "fa_mask.h"
+#include "fa_plan.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct fa_kargs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const float* slopes;
+    const uint8_t* mask;
+    const fa_geom* geoms;   // per-batch table (workspace) or nullptr
+    const int32_t* items;   // (b, q tile) launch list (workspace) or nullptr
+    fa_geom geom0;          // shared geometry when there is no table
+    int64_t q_bs, q_hs, q_rs;
+    int64_t kv_bs, kv_hs, kv_rs;
+    int64_t lse_bs, lse_hs;
+    int64_t m_bs, m_hs, m_rs;
+    int32_t B, N, D;
+    int32_t n_qtiles_fixed;
+    int32_t reverse_qt;
+    float scale_log2;       // scale * log2(e)
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Work item of this workgroup: heads are the fastest index, so the blocks of one (batch, head)
+// always land on the same XCD when N is a multiple of 8 (blocks go round-robin over XCDs);
+// items run heaviest first (the planner sorted the table, or reverse_qt flips the q tiles).
+__device__ __forceinline__ void fa_decode_item(const fa_kargs& a, int& b, int& h, int& qt,
+                                               fa_geom& g) {
+    const int w = blockIdx.x;
+    h = w % a.N;
+    const int item = w / a.N;
+    if (a.items) {
+        b = a.items[2 * item];
+        qt = a.items[2 * item + 1];
+        g = a.geoms[b];
+    } else {
+        const int r = item / a.B;
+        b = item % a.B;
+        qt = a.reverse_qt ? a.n_qtiles_fixed - 1 - r : r;
+        g = a.geom0;
+    }
+}
+
+__device__ __forceinline__ fa_geom fa_geom_of(const fa_kargs& a, int b) {
+    return a.geoms ? a.geoms[b] : a.geom0;
+}
+
+// ------------------------------------------------------------------------------------------
+// MFMA kernel
+// ------------------------------------------------------------------------------------------
+
+template <bool IS_BF16>
+struct mfma_io;
+
+template <>
+struct mfma_io<true> {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack(float x, float y) {
+        bf16x2 r;
+        r.x = (__bf16)x;
+        r.y = (__bf16)y;
+        return __builtin_bit_cast(uint32_t, r);
+    }
+};
+
+template <>
+struct mfma_io<false> {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack(float x, float y) {
+        f16x2 r;
+        r.x = (_Float16)x;
+        r.y = (_Float16)y;
+        return __builtin_bit_cast(uint32_t, r);
+    }
+};
+
+// LDS index (in 16-byte chunks) of chunk c of row r, for rows of 16 chunks (256 bytes).
+__device__ __forceinline__ int lds_idx16(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+// Same for rows of 8 chunks (128 bytes): two rows share a 256-byte line.
+__device__ __forceinline__ int lds_idx8(int r, int c) {
+    const int line = r >> 1;
+    return line * 16 + ((8 * (r & 1) + c) ^ (line & 7));
+}
+
+constexpr int MF_BM = FA_MFMA_BM;   // 128 query rows per workgroup
+constexpr int MF_BN = FA_MFMA_BN;   // 64 keys per tile
+constexpr int MF_THREADS = 256;
+
+template <int D, bool IS_BF16, bool ALIBI, bool DENSE>
+__global__ __attribute__((amdgpu_flat_work_group_size(MF_THREADS, MF_THREADS),
+                          amdgpu_waves_per_eu(2, 2))) void
+fa_fwd_mfma(const fa_kargs a) {
+    static_assert(D == 64 || D == 128, "MFMA path covers D = 64 and 128");
+    using io = mfma_io<IS_BF16>;
+    constexpr int KCH = D / 8;                       // 16-byte chunks per K row
+    constexpr int KSTEPS = D / 16;                   // k-steps of S^T = K Q^T
+    constexpr int DBLK = D / 32;                     // 32-row blocks of O^T
+    constexpr int KLOADS = MF_BN * KCH / MF_THREADS; // 16-byte K loads per thread
+    constexpr int VUNITS = (MF_BN / 4) * KCH;        // (4 keys x 8 d) V units per tile
+    static_assert(KLOADS >= 1 && VUNITS <= MF_THREADS, "tile shape");
+
+    __shared__ u32x4 lds_k[2][MF_BN * KCH];
+    __shared__ u32x4 lds_v[2][D * (MF_BN / 8)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int hl = lane >> 5;     // which half of the wave
+    const int ln = lane & 31;
+
+    int b, h, qt;
+    fa_geom g;
+    fa_decode_item(a, b, h, qt, g);
+    const int i0 = qt * MF_BM;
+    const int i_last = min(i0 + MF_BM, g.sq) - 1;
+    const fa_kv_range kr = fa_tile_kv_range(g, i0, i_last, MF_BN);
+
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + h * a.q_hs +
+                         int64_t(g.q_start) * a.q_rs;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.kv_bs + h * a.kv_hs +
+                         int64_t(g.kv_start) * a.kv_rs;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.kv_bs + h * a.kv_hs +
+                         int64_t(g.kv_start) * a.kv_rs;
+
+    // This lane's query row; Q^T is the B operand: lane holds d = 16 t + 8 hl .. + 7.
+    const int row = i0 + wave * 32 + ln;
+    const bool row_ok = row < g.sq;
+    u32x4 qop[KSTEPS];
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+        qop[t] = row_ok ? *reinterpret_cast<const u32x4*>(qp + int64_t(row) * a.q_rs + 16 * t + 8 * hl)
+                        : u32x4{0, 0, 0, 0};
+    }
+    const int row_lo = fa_row_lo(g, row);
+    const int row_hi = fa_row_hi(g, row);
+    const float sl2 = a.scale_log2;
+    float slope2 = 0.f;
+    if (ALIBI) slope2 = a.slopes[h] * kLog2e;
+    const int off = g.skv - g.sq;
+    const uint8_t* mrow = nullptr;
+    if (DENSE) mrow = a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs;
+
+    float m_run = -INFINITY;   // running max, log2 domain (scale folded in)
+    float l_run = 0.f;         // this lane's half of the running sum
+    f32x16 oacc[DBLK];
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
+
+    u32x4 kreg[KLOADS];
+    u32x4 vreg[4];
+
+    auto gload = [&](int kt) {
+        const int j0 = kt * MF_BN;
+#pragma unroll
+        for (int p = 0; p < KLOADS; ++p) {
+            const int ci = p * MF_THREADS + tid;
+            const int r = ci / KCH, c = ci % KCH;
+            const int j = j0 + r;
+            kreg[p] = j < g.skv ? *reinterpret_cast<const u32x4*>(kp + int64_t(j) * a.kv_rs + c * 8)
+                                : u32x4{0, 0, 0, 0};
+        }
+        if (tid < VUNITS) {
+            const int dc = tid % KCH, jq = tid / KCH;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + 4 * jq + q;
+                vreg[q] = j < g.skv ? *reinterpret_cast<const u32x4*>(vp + int64_t(j) * a.kv_rs + dc * 8)
+                                    : u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+
+    // K rows as loaded (swizzled); V transposed to V^T[d][key position], where the key order
+    // inside each group of 16 swaps bits 2 and 3 so that the 8 keys one lane needs for a
+    // PV k-step sit in one 16-byte chunk.
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < KLOADS; ++p) {
+            const int ci = p * MF_THREADS + tid;
+            const int r = ci / KCH, c = ci % KCH;
+            lds_k[buf][KCH == 16 ? lds_idx16(r, c) : lds_idx8(r, c)] = kreg[p];
+        }
+        if (tid < VUNITS) {
+            const int dc = tid % KCH, jq = tid / KCH;
+            const int jm = jq & 3;
+            const int jpos = 16 * (jq >> 2) + 8 * (jm & 1) + 4 * (jm >> 1);
+            const int cc = jpos >> 3, half = (jpos >> 2) & 1;
+            u32x2* vv = reinterpret_cast<u32x2*>(lds_v[buf]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
+                const u32x2 ev = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
+                const u32x2 od = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
+                const int d = 8 * dc + 2 * w;
+                vv[2 * lds_idx8(d, cc) + half] = ev;
+                vv[2 * lds_idx8(d + 1, cc) + half] = od;
+            }
+        }
+    };
+
+    if (kr.begin < kr.end) {
+        gload(kr.begin);
+        sstore(0);
+        __syncthreads();
+        for (int kt = kr.begin; kt < kr.end; ++kt) {
+            const int buf = (kt - kr.begin) & 1;
+            const bool has_next = kt + 1 < kr.end;
+            if (has_next) gload(kt + 1);
+
+            // S^T (keys x rows): lane holds row `row`, keys j0 + 32 jb + 8 (r/4) + 4 hl + r%4.
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+            for (int t = 0; t < KSTEPS; ++t) {
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    const int r = 32 * jb + ln;
+                    const u32x4 kop = lds_k[buf][KCH == 16 ? lds_idx16(r, 2 * t + hl) : lds_idx8(r, 2 * t + hl)];
+                    sacc[jb] = io::mma(kop, qop[t], sacc[jb]);
+                }
+            }
+            const int j0 = kt * MF_BN;
+            float s[32];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) s[e] = sacc[e >> 4][e & 15];
+
+            const bool full = !DENSE && fa_tile_full(g, i0, i_last, j0, MF_BN);
+            if (!full) {
+                if (DENSE) {
+#pragma unroll
+                    for (int e = 0; e < 32; ++e) {
+                        const int r = e & 15;
+                        const int j = j0 + 32 * (e >> 4) + 8 * (r >> 2) + 4 * hl + (r & 3);
+                        const bool vis = row_ok && j < g.skv && mrow[j] == 0;
+                        s[e] = vis ? s[e] : -INFINITY;
+                    }
+                } else {
+                    const int lo_rel = row_lo - j0 - 4 * hl;
+                    const int hi_rel = row_hi - j0 - 4 * hl;
+#pragma unroll
+                    for (int e = 0; e < 32; ++e) {
+                        const int r = e & 15;
+                        const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
+                        s[e] = (kc >= lo_rel && kc <= hi_rel) ? s[e] : -INFINITY;
+                    }
+                }
+            }
+            float mx = -INFINITY;
+            if (ALIBI) {
+                const float base = slope2 * float(j0 + 4 * hl - row - off);
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    const int r = e & 15;
+                    const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
+                    s[e] = fmaf(s[e], sl2, fmaf(slope2, float(kc), base));
+                    mx = fmaxf(mx, s[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) mx = fmaxf(mx, s[e]);
+                mx *= sl2;
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // Rescale only when the row maximum grows by more than 2^8: p stays <= 256, and the
+            // final O / l and LSE do not depend on which maximum was used.
+            const bool need = mx > m_run + 8.f;
+            if (__any(need)) {
+                const float alpha = need ? exp2f(m_run - mx) : 1.f;
+                if (need) m_run = mx;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            float p[32];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                p[e] = ALIBI ? __builtin_amdgcn_exp2f(s[e] - m_use)
+                             : __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -m_use));
+                l_run += p[e];
+            }
+            // P^T as the B operand: k-step t takes accumulator entries 8 (t%2) .. +7 of block t/2.
+            u32x4 pop[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int base = 16 * (t >> 1) + 8 * (t & 1);
+                pop[t] = u32x4{io::pack(p[base + 0], p[base + 1]), io::pack(p[base + 2], p[base + 3]),
+                               io::pack(p[base + 4], p[base + 5]), io::pack(p[base + 6], p[base + 7])};
+            }
+            // O^T (d x rows) += V^T P^T.
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const u32x4 vop = lds_v[buf][lds_idx8(32 * db + ln, 2 * t + hl)];
+                    oacc[db] = io::mma(vop, pop[t], oacc[db]);
+                }
+            }
+            if (has_next) sstore(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: O = O / l, LSE = ln2 (m + log2 l); rows with nothing visible give 0 and -inf.
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (row_ok) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (hl == 0) {
+            a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + row] =
+                l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        }
+        uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.q_bs + h * a.q_hs +
+                       (int64_t(g.q_start) + row) * a.q_rs;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int d = 32 * db + 8 * gi + 4 * hl;
+                const u32x2 w = {io::pack(oacc[db][4 * gi + 0] * inv, oacc[db][4 * gi + 1] * inv),
+                                 io::pack(oacc[db][4 * gi + 2] * inv, oacc[db][4 * gi + 3] * inv)};
+                *reinterpret_cast<u32x2*>(op + d) = w;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Generic kernel: fp32 arithmetic, any dtype, D <= DMAX.
+// ------------------------------------------------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) {
+    return float(x);
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x) {
+    return T(x);
+}
+
+constexpr int GN_BM = FA_GEN_BM;   // 64 query rows per workgroup (one wave)
+constexpr int GN_BN = FA_GEN_BN;   // 16 keys per tile
+
+template <typename T, int DMAX>
+__global__ __launch_bounds__(GN_BM) void fa_fwd_generic(const fa_kargs a, int dense, int alibi) {
+    // Q rows of this workgroup (padded by one float so each thread's row starts on its own
+    // bank) and one K/V tile, all in fp32. Only the O accumulator lives in registers.
+    __shared__ float qs[GN_BM][DMAX + 1];
+    __shared__ float ks[GN_BN][DMAX];
+    __shared__ float vs[GN_BN][DMAX];
+    const int tid = threadIdx.x;
+    const int D = a.D;
+    int b, h, qt;
+    fa_geom g;
+    fa_decode_item(a, b, h, qt, g);
+    const int i0 = qt * GN_BM;
+    const int i_last = min(i0 + GN_BM, g.sq) - 1;
+    const fa_kv_range kr = fa_tile_kv_range(g, i0, i_last, GN_BN);
+    const T* qp = static_cast<const T*>(a.q) + b * a.q_bs + h * a.q_hs + int64_t(g.q_start) * a.q_rs;
+    const T* kp = static_cast<const T*>(a.k) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+    const T* vp = static_cast<const T*>(a.v) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+
+    for (int e = tid; e < GN_BM * DMAX; e += GN_BM) {
+        const int r = e / DMAX, d = e % DMAX;
+        const int i = i0 + r;
+        qs[r][d] = (i < g.sq && d < D) ? to_f32(qp[int64_t(i) * a.q_rs + d]) : 0.f;
+    }
+    const int row = i0 + tid;
+    const bool row_ok = row < g.sq;
+    float o[DMAX];
+#pragma unroll
+    for (int d = 0; d < DMAX; ++d) o[d] = 0.f;
+    const int row_lo = fa_row_lo(g, row), row_hi = fa_row_hi(g, row);
+    const float slope2 = alibi ? a.slopes[h] * kLog2e : 0.f;
+    const int off = g.skv - g.sq;
+    const uint8_t* mrow = dense ? a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs
+                                : nullptr;
+    float m = -INFINITY, l = 0.f;
+    for (int kt = kr.begin; kt < kr.end; ++kt) {
+        const int j0 = kt * GN_BN;
+        __syncthreads();   // previous tile fully consumed (and, first time, Q staged)
+        for (int e = tid; e < GN_BN * DMAX; e += GN_BM) {
+            const int r = e / DMAX, d = e % DMAX;
+            const int j = j0 + r;
+            const bool ok = j < g.skv && d < D;
+            ks[r][d] = ok ? to_f32(kp[int64_t(j) * a.kv_rs + d]) : 0.f;
+            vs[r][d] = ok ? to_f32(vp[int64_t(j) * a.kv_rs + d]) : 0.f;
+        }
+        __syncthreads();
+        // One key at a time: running max m, running sum l, O rescaled when m grows.
+#pragma unroll 1
+        for (int jj = 0; jj < GN_BN; ++jj) {
+            float dot = 0.f;
+#pragma unroll
+            for (int d = 0; d < DMAX; ++d) dot = fmaf(qs[tid][d], ks[jj][d], dot);
+            const int j = j0 + jj;
+            const bool vis = dense ? (row_ok && j < g.skv && mrow[j] == 0) : (j >= row_lo && j <= row_hi);
+            float sv = dot * a.scale_log2;
+            if (alibi) sv += slope2 * float(j - row - off);
+            sv = vis ? sv : -INFINITY;
+            const float m_new = fmaxf(m, sv);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = exp2f(m - m_use);
+            const float pj = exp2f(sv - m_use);
+            l = fmaf(l, alpha, pj);
+#pragma unroll
+            for (int d = 0; d < DMAX; ++d) o[d] = fmaf(o[d], alpha, pj * vs[jj][d]);
+            m = m_new;
+        }
+    }
+    if (row_ok) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+        T* op = static_cast<T*>(a.o) + b * a.q_bs + h * a.q_hs + (int64_t(g.q_start) + row) * a.q_rs;
+#pragma unroll
+        for (int d = 0; d < DMAX; ++d)
+            if (d < D) op[d] = from_f32<T>(o[d] * inv);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Mask probe kernels: the same mask code, no attention arithmetic.
+// ------------------------------------------------------------------------------------------
+
+__global__ void fa_probe_rows(const fa_kargs a, int64_t* counts, int dense) {
+    const int b = blockIdx.x, h = blockIdx.y;
+    const fa_geom g = fa_geom_of(a, b);
+    for (int i = threadIdx.x; i < g.sq; i += blockDim.x) {
+        int64_t cnt = 0;
+        if (dense) {
+            const uint8_t* mrow = a.mask + b * a.m_bs + h * a.m_hs + int64_t(i) * a.m_rs;
+            for (int j = 0; j < g.skv; ++j) cnt += mrow[j] == 0;
+        } else {
+            const int lo = fa_row_lo(g, i), hi = fa_row_hi(g, i);
+            cnt = hi >= lo ? hi - lo + 1 : 0;
+        }
+        counts[b * a.lse_bs + h * a.lse_hs + g.q_start + i] = cnt;
+    }
+}
+
+__global__ void fa_probe_tiles(const fa_kargs a, uint8_t* tile_class, int64_t n_kv_max, int bm,
+                               int bn) {
+    const int qt = blockIdx.x, b = blockIdx.y;
+    const fa_geom g = fa_geom_of(a, b);
+    const int nqt = (g.sq + bm - 1) / bm;
+    if (qt >= nqt) return;
+    int64_t r = qt;
+    for (int bb = 0; bb < b; ++bb) r += (fa_geom_of(a, bb).sq + bm - 1) / bm;
+    const int i0 = qt * bm, i1 = min(i0 + bm, g.sq) - 1;
+    const fa_kv_range kr = fa_tile_kv_range(g, i0, i1, bn);
+    const int nkv = (g.skv + bn - 1) / bn;
+    for (int kt = threadIdx.x; kt < n_kv_max; kt += blockDim.x) {
+        uint8_t cls;
+        if (kt >= nkv) cls = 3;
+        else if (kt < kr.begin || kt >= kr.end) cls = 0;
+        else cls = fa_tile_full(g, i0, i1, kt * bn, bn) ? 2 : 1;
+        tile_class[r * n_kv_max + kt] = cls;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Host side
+// ------------------------------------------------------------------------------------------
+
+fa_kargs make_kargs(const fa_plan& p, const void* q, const void* k, const void* v, void* out,
+                    float* lse, const float* slopes, const uint8_t* mask, void* workspace,
+                    float scale) {
+    fa_kargs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = out;
+    a.lse = lse;
+    a.slopes = slopes;
+    a.mask = mask;
+    if (p.table) {
+        a.geoms = static_cast<const fa_geom*>(workspace);
+        a.items = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + p.ws_items_offset);
+    }
+    a.geom0 = p.geom0;
+    a.q_bs = p.q_bs; a.q_hs = p.q_hs; a.q_rs = p.q_rs;
+    a.kv_bs = p.kv_bs; a.kv_hs = p.kv_hs; a.kv_rs = p.kv_rs;
+    a.lse_bs = p.lse_bs; a.lse_hs = p.lse_hs;
+    a.m_bs = p.m_bs; a.m_hs = p.m_hs; a.m_rs = p.m_rs;
+    a.B = p.B;
+    a.N = p.N;
+    a.D = p.D;
+    a.n_qtiles_fixed = p.n_qtiles_fixed;
+    a.reverse_qt = p.reverse_qt;
+    a.scale_log2 = scale * kLog2e;
+    return a;
+}
+
+bool log_enabled() {
+    const char* e = std::getenv("FA_LOG");
+    return e && e[0] == '1';
+}
+
+fa_status upload_tables(const fa_plan& p, void* workspace, hipStream_t stream) {
+    if (!p.table || p.ws_bytes == 0) return FA_OK;
+    // The image is pageable host memory; hipMemcpyAsync stages it before returning.
+    std::vector<unsigned char> image;
+    fa_plan_workspace_image(p, &image);
+    if (hipMemcpyAsync(workspace, image.data(), image.size(), hipMemcpyHostToDevice, stream) != hipSuccess)
+        return FA_ERR_HIP;
+    return FA_OK;
+}
+
+template <int D, bool BF>
+void launch_mfma_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipStream_t s) {
+    const dim3 block(MF_THREADS);
+    if (alibi) {
+        if (dense) fa_fwd_mfma<D, BF, true, true><<<grid, block, 0, s>>>(a);
+        else fa_fwd_mfma<D, BF, true, false><<<grid, block, 0, s>>>(a);
+    } else {
+        if (dense) fa_fwd_mfma<D, BF, false, true><<<grid, block, 0, s>>>(a);
+        else fa_fwd_mfma<D, BF, false, false><<<grid, block, 0, s>>>(a);
+    }
+}
+
+template <typename T>
+void launch_generic_t(const fa_kargs& a, int D, bool alibi, bool dense, dim3 grid, hipStream_t s) {
+    const dim3 block(GN_BM);
+    if (D <= 32) fa_fwd_generic<T, 32><<<grid, block, 0, s>>>(a, dense, alibi);
+    else if (D <= 64) fa_fwd_generic<T, 64><<<grid, block, 0, s>>>(a, dense, alibi);
+    else fa_fwd_generic<T, 128><<<grid, block, 0, s>>>(a, dense, alibi);
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* out,
+                            float* softmax_lse, const fa_dims* dims, int32_t layout,
+                            int32_t sparse_mode, int64_t pre_tokens, int64_t next_tokens,
+                            const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                            const int64_t* prefix, const float* alibi_slopes,
+                            const uint8_t* atten_mask, const int64_t* mask_bcast, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = sparse_mode;
+    c.pre_tokens = pre_tokens;
+    c.next_tokens = next_tokens;
+    c.actual_seq_qlen = actual_seq_qlen;
+    c.actual_seq_kvlen = actual_seq_kvlen;
+    c.prefix = prefix;
+    c.has_alibi = alibi_slopes != nullptr;
+    c.has_mask = atten_mask != nullptr;
+    c.mask_bcast = mask_bcast;
+    c.scale = scale;
+    fa_plan p;
+    fa_status st = fa_make_plan(c, true, &p);
+    if (st != FA_OK) return st;
+    if (!p.empty) {
+        if (!q || !out || !softmax_lse) return FA_ERR_NULLPTR;
+        if (p.kv_total > 0 && (!k || !v)) return FA_ERR_NULLPTR;
+    }
+    if (p.ws_bytes > 0) {
+        if (!workspace) return FA_ERR_NULLPTR;
+        if (workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+    }
+    if (p.empty) return FA_OK;
+    const int64_t nblocks = p.n_items * p.N;
+    if (nblocks >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (log_enabled()) {
+        std::fprintf(stderr,
+                     "[fa] kernel=%s bm=%d bn=%d items/head=%lld blocks=%lld kv tiles visited/full/"
+                     "dense=%lld/%lld/%lld table=%d reverse=%d ws=%zu\n",
+                     p.kernel == FA_KERNEL_MFMA ? "mfma" : "generic", p.bm, p.bn,
+                     (long long)p.n_items, (long long)nblocks, (long long)p.kv_tiles_visited,
+                     (long long)p.kv_tiles_full, (long long)p.kv_tiles_total, int(p.table),
+                     p.reverse_qt, p.ws_bytes);
+    }
+    st = upload_tables(p, workspace, s);
+    if (st != FA_OK) return st;
+    const fa_kargs a = make_kargs(p, q, k, v, out, softmax_lse, alibi_slopes, atten_mask, workspace, scale);
+    const dim3 grid(static_cast<unsigned>(nblocks));
+    const bool alibi = alibi_slopes != nullptr;
+    const bool dense = sparse_mode == 1;
+    (void)hipGetLastError();
+    if (p.kernel == FA_KERNEL_MFMA) {
+        const bool bf = dims->dtype == FA_DTYPE_BF16;
+        if (p.D == 128) {
+            if (bf) launch_mfma_d<128, true>(a, alibi, dense, grid, s);
+            else launch_mfma_d<128, false>(a, alibi, dense, grid, s);
+        } else {
+            if (bf) launch_mfma_d<64, true>(a, alibi, dense, grid, s);
+            else launch_mfma_d<64, false>(a, alibi, dense, grid, s);
+        }
+    } else {
+        switch (dims->dtype) {
+            case FA_DTYPE_F32: launch_generic_t<float>(a, p.D, alibi, dense, grid, s); break;
+            case FA_DTYPE_F16: launch_generic_t<_Float16>(a, p.D, alibi, dense, grid, s); break;
+            default: launch_generic_t<__bf16>(a, p.D, alibi, dense, grid, s); break;
+        }
+    }
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    return FA_OK;
+}
+
+extern "C" fa_status fa_mask_probe(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                                   int64_t pre_tokens, int64_t next_tokens,
+                                   const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                                   const int64_t* prefix, const uint8_t* atten_mask,
+                                   const int64_t* mask_bcast, int64_t* row_visible_counts,
+                                   uint8_t* tile_class, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = sparse_mode;
+    c.pre_tokens = pre_tokens;
+    c.next_tokens = next_tokens;
+    c.actual_seq_qlen = actual_seq_qlen;
+    c.actual_seq_kvlen = actual_seq_kvlen;
+    c.prefix = prefix;
+    c.has_mask = atten_mask != nullptr;
+    c.mask_bcast = mask_bcast;
+    c.check_scale = false;
+    fa_plan p;
+    fa_status st = fa_make_plan(c, true, &p);
+    if (st != FA_OK) return st;
+    if (sparse_mode == 1 && tile_class) return FA_ERR_PARAM_INVALID;
+    if (!p.empty && !row_visible_counts) return FA_ERR_NULLPTR;
+    if (p.ws_bytes > 0) {
+        if (!workspace) return FA_ERR_NULLPTR;
+        if (workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+    }
+    if (p.empty || p.B == 0) return FA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = upload_tables(p, workspace, s);
+    if (st != FA_OK) return st;
+    const fa_kargs a = make_kargs(p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, atten_mask,
+                                  workspace, 1.0f);
+    (void)hipGetLastError();
+    fa_probe_rows<<<dim3(p.B, p.N), dim3(256), 0, s>>>(a, row_visible_counts, sparse_mode == 1);
+    if (tile_class && p.n_kvtiles_max > 0) {
+        int64_t max_nqt = 0;
+        for (const fa_geom& g : p.geoms) max_nqt = std::max<int64_t>(max_nqt, (g.sq + p.bm - 1) / p.bm);
+        if (max_nqt > 0)
+            fa_probe_tiles<<<dim3(unsigned(max_nqt), p.B), dim3(256), 0, s>>>(a, tile_class, p.n_kvtiles_max,
+                                                                            p.bm, p.bn);
+    }
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    return FA_OK;
+}

@@ -1,0 +1,384 @@
+// fa_plan.cpp - host-side validation and planning (no HIP dependency).
+//
+// Validation follows the rules the pages state, in "sparseMode介绍":
+//   sparseMode=0: negative nextTokens needs preTokens >= |nextTokens| and |nextTokens| < Skv;
+//                 negative preTokens needs nextTokens >= |preTokens| and |preTokens| < Sq.
+//   sparseMode=4: preTokens and nextTokens must intersect (read as pre + next >= 0).
+//   sparseMode=7: band batch: preTokens >= last_Skv, last_Sq - last_Skv <= nextTokens <= 0;
+//                 other batches Sq <= Skv; the optional pse (bias) input is not supported.
+//   sparseMode=8: band batch: preTokens >= first_Skv, nextTokens >= first_Sq - first_Skv;
+//                 no pse.
+// and in "压缩mask" (constraints): alibi needs a head size of at most 128.
+// Every check runs before any device work, as the return-code table of the
+// "aclnnScatterPaKvCache" doc describes for its first phase.
+#include "fa_plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+namespace {
+
+int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool mfma_eligible(int32_t dtype, int64_t D) {
+    return (dtype == FA_DTYPE_F16 || dtype == FA_DTYPE_BF16) && (D == 64 || D == 128);
+}
+
+}  // namespace
+
+static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool sizes_only,
+                                fa_plan* out) {
+    if (!call.dims || !out) return FA_ERR_NULLPTR;
+    const fa_dims& d = *call.dims;
+    const int mode = call.sparse_mode;
+    const bool tnd = call.layout == FA_LAYOUT_TND;
+
+    if (d.dtype < FA_DTYPE_F32 || d.dtype > FA_DTYPE_BF16) return FA_ERR_PARAM_INVALID;
+    if (call.layout < FA_LAYOUT_BNSD || call.layout > FA_LAYOUT_TND) return FA_ERR_PARAM_INVALID;
+    if (mode < 0 || mode > 8) return FA_ERR_PARAM_INVALID;
+    if (d.B < 0 || d.N < 1 || d.D < 1) return FA_ERR_PARAM_INVALID;
+    if (d.B > (int64_t(1) << 24) || d.N > (int64_t(1) << 16)) return FA_ERR_UNSUPPORTED;
+    if ((mode == 7 || mode == 8) && !tnd) return FA_ERR_PARAM_INVALID;
+    if (!sizes_only) {
+        if (call.check_scale && !(std::isfinite(call.scale) && call.scale > 0.0f))
+            return FA_ERR_PARAM_INVALID;
+        if (call.has_alibi && d.D > 128) return FA_ERR_PARAM_INVALID;
+        if (call.has_alibi && (mode == 7 || mode == 8)) return FA_ERR_PARAM_INVALID;
+        if (mode == 1 && !call.has_mask) return FA_ERR_NULLPTR;
+    }
+    if (mode == 1 && tnd) return FA_ERR_UNSUPPORTED;
+    if (d.D > 128) return FA_ERR_UNSUPPORTED;
+
+    const int64_t B = d.B;
+    std::vector<int64_t> sq(B), skv(B), qs(B), ks(B);
+    if (tnd) {
+        if (B > 0 && (!call.actual_seq_qlen || !call.actual_seq_kvlen)) return FA_ERR_NULLPTR;
+        int64_t pq = 0, pk = 0;
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t cq = call.actual_seq_qlen[b], ck = call.actual_seq_kvlen[b];
+            if (cq < pq || ck < pk) return FA_ERR_PARAM_INVALID;  // cumulative ends only grow
+            qs[b] = pq;
+            ks[b] = pk;
+            sq[b] = cq - pq;
+            skv[b] = ck - pk;
+            if (sq[b] >= FA_MAX_SEQ || skv[b] >= FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
+            pq = cq;
+            pk = ck;
+        }
+        if (pq != d.T_q || pk != d.T_kv) return FA_ERR_PARAM_INVALID;
+        if (d.T_q >= (int64_t(1) << 31) || d.T_kv >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+    } else {
+        if (d.Sq < 0 || d.Skv < 0) return FA_ERR_PARAM_INVALID;
+        if (d.Sq >= FA_MAX_SEQ || d.Skv >= FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
+        for (int64_t b = 0; b < B; ++b) {
+            sq[b] = d.Sq;
+            skv[b] = d.Skv;
+            qs[b] = ks[b] = 0;
+        }
+    }
+    // Element counts must stay well inside int64.
+    {
+        const double rows = tnd ? double(d.T_q) : double(B) * double(d.Sq);
+        const double keys = tnd ? double(d.T_kv) : double(B) * double(d.Skv);
+        const double big = std::ldexp(1.0, 60);
+        if (rows * double(d.N) * double(d.D) > big || keys * double(d.N) * double(d.D) > big)
+            return FA_ERR_UNSUPPORTED;
+    }
+    int64_t max_sq = 0, max_skv = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        max_sq = std::max(max_sq, sq[b]);
+        max_skv = std::max(max_skv, skv[b]);
+    }
+
+    // Mode-specific arguments.
+    const int64_t pre = call.pre_tokens, nxt = call.next_tokens;
+    const bool band_mode = mode == 0 || mode == 4 || mode == 7 || mode == 8;
+    const int64_t huge = int64_t(1) << 62;
+    int64_t band_b = -1;
+    if (mode == 7 || mode == 8) {
+        for (int64_t b = 0; b < B; ++b) {
+            if (sq[b] > 0 && skv[b] > 0) {
+                band_b = b;
+                if (mode == 8) break;
+            }
+        }
+    }
+    if (!sizes_only) {
+        if (band_mode && (pre < -huge || nxt < -huge)) return FA_ERR_PARAM_INVALID;
+        if (mode == 0) {
+            if (nxt < 0 && !(pre >= -nxt && -nxt < max_skv)) return FA_ERR_PARAM_INVALID;
+            if (pre < 0 && !(nxt >= -pre && -pre < max_sq)) return FA_ERR_PARAM_INVALID;
+        }
+        if (mode == 4 && clamp64(pre, -huge, huge) + clamp64(nxt, -huge, huge) < 0)
+            return FA_ERR_PARAM_INVALID;
+        if (mode == 7) {
+            for (int64_t b = 0; b < B; ++b) {
+                if (b == band_b) {
+                    if (!(pre >= skv[b] && sq[b] - skv[b] <= nxt && nxt <= 0))
+                        return FA_ERR_PARAM_INVALID;
+                } else if (sq[b] > skv[b]) {
+                    return FA_ERR_PARAM_INVALID;
+                }
+            }
+        }
+        if (mode == 8 && band_b >= 0) {
+            if (!(pre >= skv[band_b] && nxt >= sq[band_b] - skv[band_b])) return FA_ERR_PARAM_INVALID;
+        }
+        if (mode == 5 || mode == 6) {
+            if (B > 0 && !call.prefix) return FA_ERR_NULLPTR;
+            for (int64_t b = 0; b < B; ++b)
+                if (call.prefix[b] < 0) return FA_ERR_PARAM_INVALID;
+        }
+    }
+
+    fa_plan p;
+    p.B = int32_t(B);
+    p.N = int32_t(d.N);
+    p.D = int32_t(d.D);
+    p.kernel = mfma_eligible(d.dtype, d.D) ? FA_KERNEL_MFMA : FA_KERNEL_GENERIC;
+    p.bm = p.kernel == FA_KERNEL_MFMA ? FA_MFMA_BM : FA_GEN_BM;
+    p.bn = p.kernel == FA_KERNEL_MFMA ? FA_MFMA_BN : FA_GEN_BN;
+    for (int64_t b = 0; b < B; ++b) {
+        p.rows_total += sq[b];
+        p.kv_total += skv[b];
+    }
+    p.empty = p.rows_total == 0;
+
+    // Geometry per batch (see fa_mask.h for the a / c / f rule table).
+    const int32_t prei = int32_t(clamp64(pre, -FA_LIM, FA_LIM));
+    const int32_t nxti = int32_t(clamp64(nxt, -FA_LIM, FA_LIM));
+    p.geoms.resize(B);
+    for (int64_t b = 0; b < B; ++b) {
+        fa_geom g{};
+        g.q_start = int32_t(qs[b]);
+        g.kv_start = int32_t(ks[b]);
+        g.sq = int32_t(sq[b]);
+        g.skv = int32_t(skv[b]);
+        const int32_t off = g.skv - g.sq;
+        int m = mode;
+        if (m == 7) m = (b == band_b) ? 4 : 3;
+        if (m == 8) m = (b == band_b) ? 4 : 2;
+        g.f = -FA_BIG;
+        switch (m) {
+            case 0: g.a = -prei; g.c = nxti; break;
+            case 1: g.a = -FA_BIG; g.c = FA_BIG; break;
+            case 2: g.a = -FA_BIG; g.c = 0; break;
+            case 3: g.a = -FA_BIG; g.c = off; break;
+            case 4: g.a = off - prei; g.c = off + nxti; break;
+            default: {  // 5, 6
+                g.a = -FA_BIG;
+                g.c = off;
+                const int64_t pl = sizes_only ? 0 : std::min<int64_t>(call.prefix[b], g.skv);
+                g.f = int32_t(pl) - 1;
+                break;
+            }
+        }
+        p.geoms[b] = g;
+    }
+    if (B > 0) p.geom0 = p.geoms[0];
+
+    // Strides (elements).
+    const int64_t N = d.N, D = d.D;
+    if (call.layout == FA_LAYOUT_BNSD) {
+        p.q_bs = N * d.Sq * D; p.q_hs = d.Sq * D; p.q_rs = D;
+        p.kv_bs = N * d.Skv * D; p.kv_hs = d.Skv * D; p.kv_rs = D;
+    } else if (call.layout == FA_LAYOUT_BSND) {
+        p.q_bs = d.Sq * N * D; p.q_hs = D; p.q_rs = N * D;
+        p.kv_bs = d.Skv * N * D; p.kv_hs = D; p.kv_rs = N * D;
+    } else {
+        p.q_bs = 0; p.q_hs = D; p.q_rs = N * D;
+        p.kv_bs = 0; p.kv_hs = D; p.kv_rs = N * D;
+    }
+    if (tnd) {
+        p.lse_bs = 0; p.lse_hs = d.T_q;
+    } else {
+        p.lse_bs = N * d.Sq; p.lse_hs = d.Sq;
+    }
+    if (mode == 1) {
+        const bool bb = call.mask_bcast && call.mask_bcast[0] != 0;
+        const bool hb = call.mask_bcast && call.mask_bcast[1] != 0;
+        const int64_t nm = hb ? 1 : N;
+        p.m_rs = d.Skv;
+        p.m_hs = hb ? 0 : d.Sq * d.Skv;
+        p.m_bs = bb ? 0 : nm * d.Sq * d.Skv;
+    }
+
+    // Work items.
+    p.table = tnd || mode == 5 || mode == 6;
+    p.n_qtiles_total = 0;
+    p.n_kvtiles_max = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        p.n_qtiles_total += ceil_div(sq[b], p.bm);
+        p.n_kvtiles_max = std::max(p.n_kvtiles_max, ceil_div(skv[b], p.bn));
+    }
+    auto item_cost = [&](int64_t b, int64_t qt, int64_t* full) -> int64_t {
+        const fa_geom& g = p.geoms[b];
+        const int32_t i0 = int32_t(qt * p.bm);
+        const int32_t i1 = std::min<int32_t>(i0 + p.bm, g.sq) - 1;
+        const fa_kv_range r = fa_tile_kv_range(g, i0, i1, p.bn);
+        if (full) {
+            *full = 0;
+            if (mode != 1)
+                for (int32_t kt = r.begin; kt < r.end; ++kt)
+                    *full += fa_tile_full(g, i0, i1, kt * p.bn, p.bn) ? 1 : 0;
+        }
+        return r.end - r.begin;
+    };
+    if (p.table) {
+        p.n_items = p.n_qtiles_total;
+        if (with_tables && !sizes_only) {
+            std::vector<std::pair<int64_t, int64_t>> order;  // (cost, index)
+            std::vector<int32_t> raw;
+            order.reserve(p.n_items);
+            raw.reserve(2 * p.n_items);
+            for (int64_t b = 0; b < B; ++b) {
+                const int64_t nqt = ceil_div(sq[b], p.bm);
+                for (int64_t qt = 0; qt < nqt; ++qt) {
+                    order.push_back({item_cost(b, qt, nullptr), int64_t(raw.size() / 2)});
+                    raw.push_back(int32_t(b));
+                    raw.push_back(int32_t(qt));
+                }
+            }
+            // Longest first; ties keep batch-major order.
+            std::stable_sort(order.begin(), order.end(),
+                             [](const std::pair<int64_t, int64_t>& x,
+                                const std::pair<int64_t, int64_t>& y) { return x.first > y.first; });
+            p.items.resize(2 * order.size());
+            for (size_t n = 0; n < order.size(); ++n) {
+                p.items[2 * n] = raw[2 * order[n].second];
+                p.items[2 * n + 1] = raw[2 * order[n].second + 1];
+            }
+        }
+        p.ws_items_offset = align256(size_t(B) * sizeof(fa_geom));
+        p.ws_bytes = p.empty ? 0 : p.ws_items_offset + size_t(p.n_items) * 2 * sizeof(int32_t);
+    } else {
+        p.n_qtiles_fixed = int32_t(ceil_div(d.Sq, p.bm));
+        p.n_items = B * p.n_qtiles_fixed;
+        p.ws_bytes = 0;
+        if (B > 0 && p.n_qtiles_fixed > 1 && !sizes_only)
+            p.reverse_qt = item_cost(0, p.n_qtiles_fixed - 1, nullptr) > item_cost(0, 0, nullptr);
+    }
+
+    if (with_tables && !sizes_only) {
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t nqt = ceil_div(sq[b], p.bm);
+            for (int64_t qt = 0; qt < nqt; ++qt) {
+                int64_t full = 0;
+                p.kv_tiles_visited += item_cost(b, qt, &full);
+                p.kv_tiles_full += full;
+                p.kv_tiles_total += ceil_div(skv[b], p.bn);
+            }
+        }
+    }
+    *out = std::move(p);
+    return FA_OK;
+}
+
+fa_status fa_make_plan(const fa_call& call, bool with_tables, fa_plan* plan) {
+    return make_plan_impl(call, with_tables, false, plan);
+}
+
+fa_status fa_make_plan_sizes(const fa_call& call, fa_plan* plan) {
+    return make_plan_impl(call, false, true, plan);
+}
+
+void fa_plan_workspace_image(const fa_plan& plan, std::vector<unsigned char>* image) {
+    image->assign(plan.ws_bytes, 0);
+    if (plan.ws_bytes == 0) return;
+    std::memcpy(image->data(), plan.geoms.data(), plan.geoms.size() * sizeof(fa_geom));
+    std::memcpy(image->data() + plan.ws_items_offset, plan.items.data(),
+                plan.items.size() * sizeof(int32_t));
+}
+
+// ---------------------------------------------------------------------------------------
+// Host-only entry points of the C ABI.
+// ---------------------------------------------------------------------------------------
+
+extern "C" fa_status fa_fwd_workspace_size(const fa_dims* dims, int32_t layout,
+                                           int32_t sparse_mode, const int64_t* actual_seq_qlen,
+                                           const int64_t* actual_seq_kvlen, size_t* bytes) {
+    if (!dims || !bytes) return FA_ERR_NULLPTR;
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = sparse_mode;
+    c.actual_seq_qlen = actual_seq_qlen;
+    c.actual_seq_kvlen = actual_seq_kvlen;
+    fa_plan p;
+    const fa_status st = fa_make_plan_sizes(c, &p);
+    if (st != FA_OK) return st;
+    *bytes = p.ws_bytes;
+    return FA_OK;
+}
+
+extern "C" fa_status fa_tile_shape(const fa_dims* dims, int32_t layout,
+                                   const int64_t* actual_seq_qlen,
+                                   const int64_t* actual_seq_kvlen, int32_t* block_m,
+                                   int32_t* block_n, int64_t* n_qtiles_total,
+                                   int64_t* n_kvtiles_max) {
+    if (!dims || !block_m || !block_n || !n_qtiles_total || !n_kvtiles_max) return FA_ERR_NULLPTR;
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = 3;
+    c.actual_seq_qlen = actual_seq_qlen;
+    c.actual_seq_kvlen = actual_seq_kvlen;
+    fa_plan p;
+    const fa_status st = fa_make_plan_sizes(c, &p);
+    if (st != FA_OK) return st;
+    *block_m = p.bm;
+    *block_n = p.bn;
+    *n_qtiles_total = p.n_qtiles_total;
+    *n_kvtiles_max = p.n_kvtiles_max;
+    return FA_OK;
+}
+
+extern "C" fa_status fa_plan_stats_get(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                                       int64_t pre_tokens, int64_t next_tokens,
+                                       const int64_t* actual_seq_qlen,
+                                       const int64_t* actual_seq_kvlen, const int64_t* prefix,
+                                       int32_t has_alibi, int32_t has_mask, float scale,
+                                       fa_plan_stats* out) {
+    if (!dims || !out) return FA_ERR_NULLPTR;
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = sparse_mode;
+    c.pre_tokens = pre_tokens;
+    c.next_tokens = next_tokens;
+    c.actual_seq_qlen = actual_seq_qlen;
+    c.actual_seq_kvlen = actual_seq_kvlen;
+    c.prefix = prefix;
+    c.has_alibi = has_alibi != 0;
+    c.has_mask = has_mask != 0;
+    c.scale = scale;
+    fa_plan p;
+    const fa_status st = fa_make_plan(c, true, &p);
+    if (st != FA_OK) return st;
+    out->kernel = p.kernel;
+    out->block_m = p.bm;
+    out->block_n = p.bn;
+    out->work_items = p.n_items;
+    out->kv_tiles_visited = p.kv_tiles_visited;
+    out->kv_tiles_full = p.kv_tiles_full;
+    out->kv_tiles_total = p.kv_tiles_total;
+    out->workspace_bytes = p.ws_bytes;
+    return FA_OK;
+}
+
+extern "C" const char* fa_status_str(fa_status status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULLPTR: return "FA_ERR_NULLPTR: a required pointer is NULL";
+        case FA_ERR_PARAM_INVALID: return "FA_ERR_PARAM_INVALID: an argument breaks a stated rule";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid but not built";
+        case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace too small";
+        default: return "unknown fa_status";
+    }
+}

@@ -1,0 +1,77 @@
+// fa_plan.h - host-side validation and planning for fa_fwd / fa_mask_probe.
+//
+// Pure C++17, no HIP include, so it can be built and tested on a machine without a GPU.
+#ifndef FA_PLAN_H_
+#define FA_PLAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/fa.h"
+#include "fa_mask.h"
+
+// Everything fa_fwd receives that the host can look at (device pointers only as flags).
+struct fa_call {
+    const fa_dims* dims = nullptr;
+    int32_t layout = 0;
+    int32_t sparse_mode = 0;
+    int64_t pre_tokens = 0, next_tokens = 0;
+    const int64_t* actual_seq_qlen = nullptr;
+    const int64_t* actual_seq_kvlen = nullptr;
+    const int64_t* prefix = nullptr;
+    bool has_alibi = false;
+    bool has_mask = false;
+    const int64_t* mask_bcast = nullptr;
+    float scale = 1.0f;
+    bool check_scale = true;
+};
+
+// Kernel families and their tiles.
+enum { FA_KERNEL_GENERIC = 0, FA_KERNEL_MFMA = 1 };
+constexpr int FA_MFMA_BM = 128;
+constexpr int FA_MFMA_BN = 64;
+constexpr int FA_GEN_BM = 64;
+constexpr int FA_GEN_BN = 16;
+
+struct fa_plan {
+    int32_t kernel = FA_KERNEL_GENERIC;
+    int32_t bm = 0, bn = 0;
+    int32_t B = 0, N = 0, D = 0;
+    int64_t rows_total = 0;     // query rows over all batches (per head)
+    int64_t kv_total = 0;       // key rows over all batches (per head)
+    bool empty = false;         // nothing to compute or write
+    // Geometry: one entry per batch; geom0 when every batch shares it.
+    std::vector<fa_geom> geoms;
+    fa_geom geom0{};
+    bool table = false;         // per-batch geometry + work-item list travel in the workspace
+    std::vector<int32_t> items; // (b, q tile) pairs in launch order (table mode)
+    int64_t n_items = 0;        // work items per head
+    int32_t n_qtiles_fixed = 0; // q tiles per batch (fixed-length mode)
+    int32_t reverse_qt = 0;     // fixed-length mode: launch the last q tiles first
+    int64_t n_qtiles_total = 0; // batch-major q tiles over all batches
+    int64_t n_kvtiles_max = 0;
+    size_t ws_bytes = 0;
+    size_t ws_items_offset = 0;
+    // Strides in elements.
+    int64_t q_bs = 0, q_hs = 0, q_rs = 0;
+    int64_t kv_bs = 0, kv_hs = 0, kv_rs = 0;
+    int64_t lse_bs = 0, lse_hs = 0;
+    int64_t m_bs = 0, m_hs = 0, m_rs = 0;
+    // Statistics (per head).
+    int64_t kv_tiles_visited = 0, kv_tiles_full = 0, kv_tiles_total = 0;
+};
+
+// Validates `call` against the pages' rules and this ABI; on success fills `plan`.
+// with_tables: also build the work-item list and tile statistics.
+fa_status fa_make_plan(const fa_call& call, bool with_tables, fa_plan* plan);
+
+// Size-only planning for the workspace-size query: checks sizes and layout, not the
+// mode-specific arguments (pre/next, prefix, mask), and builds no work-item list.
+fa_status fa_make_plan_sizes(const fa_call& call, fa_plan* plan);
+
+// Serialises the per-batch geometry and work items into a host image of the workspace.
+void fa_plan_workspace_image(const fa_plan& plan, std::vector<unsigned char>* image);
+
+#endif  // FA_PLAN_H_

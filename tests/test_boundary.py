@@ -1,0 +1,289 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every declared entry
+point, validates arguments with the documented status codes before any device work, and
+its host-side tile planning agrees with brute force over the oracle's mask."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from masked_attention_forward_amd import binding as fb
+from masked_attention_forward_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULLPTR, INVALID, UNSUPPORTED, HIPERR, WORKSPACE = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fb.load_library()
+
+
+def declared_functions():
+    names = []
+    for hdr in os.listdir(os.path.join(ROOT, "include")):
+        if not hdr.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", hdr)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"fa_fwd", "fa_fwd_workspace_size", "fa_mask_probe", "fa_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert fb.fa_status_str(code).startswith(fb.STATUS_NAMES[code])
+
+
+def _stats_status(lib, dims, layout, mode, pre=0, nxt=0, qlen=None, kvlen=None, prefix=None,
+                  alibi=False, mask=False, scale=0.125):
+    s = fb.FaPlanStats()
+    return lib.fa_plan_stats_get(ctypes.byref(dims) if dims is not None else None, layout, mode, pre, nxt,
+                                 fb._i64(qlen), fb._i64(kvlen), fb._i64(prefix), int(alibi), int(mask),
+                                 scale, ctypes.byref(s))
+
+
+def bnsd(B=2, N=4, Sq=64, Skv=64, D=128, dtype=2):
+    return fb.make_dims(dtype, 0, B=B, N=N, Sq=Sq, Skv=Skv, D=D)
+
+
+def tnd(qlens, kvlens, N=2, D=128, dtype=2):
+    return fb.make_dims(dtype, 2, B=len(qlens), N=N, D=D, T_q=sum(qlens), T_kv=sum(kvlens))
+
+
+def test_generic_validation(lib):
+    assert _stats_status(lib, None, 0, 3) == NULLPTR
+    assert _stats_status(lib, bnsd(dtype=7), 0, 3) == INVALID
+    assert _stats_status(lib, bnsd(), 5, 3) == INVALID
+    assert _stats_status(lib, bnsd(), 0, 9) == INVALID
+    assert _stats_status(lib, bnsd(), 0, -1) == INVALID
+    assert _stats_status(lib, bnsd(N=0), 0, 3) == INVALID
+    assert _stats_status(lib, bnsd(Sq=-1), 0, 3) == INVALID
+    assert _stats_status(lib, bnsd(D=256), 0, 3) == UNSUPPORTED
+    assert _stats_status(lib, bnsd(), 0, 3, scale=0.0) == INVALID
+    assert _stats_status(lib, bnsd(), 0, 3, scale=-0.1) == INVALID
+    assert _stats_status(lib, bnsd(), 0, 3, scale=float("nan")) == INVALID
+    assert _stats_status(lib, bnsd(), 0, 3) == OK
+    assert _stats_status(lib, bnsd(B=0), 0, 3) == OK
+    assert _stats_status(lib, bnsd(Sq=0, Skv=0), 0, 3) == OK
+
+
+def test_alibi_rules(lib):
+    # "压缩mask", constraints: alibi needs head size <= 128.
+    assert _stats_status(lib, bnsd(D=192), 0, 3, alibi=True) == INVALID
+    assert _stats_status(lib, bnsd(D=128), 0, 3, alibi=True) == OK
+    # "sparseMode介绍", sparseMode=7/8: the optional pse input is not supported.
+    q, k = [3, 2], [3, 6]
+    assert _stats_status(lib, tnd(q, k), 2, 7, 6, -2, synth.cumulative_ends(q), synth.cumulative_ends(k),
+                         alibi=True) == INVALID
+
+
+def test_mode0_band_sign_rules(lib):
+    """sparseMode=0: negative next needs pre >= |next| and |next| < Skv; negative pre needs
+    next >= |pre| and |pre| < Sq."""
+    d = bnsd(Sq=16, Skv=16)
+    assert _stats_status(lib, d, 0, 0, 9, -3) == OK
+    assert _stats_status(lib, d, 0, 0, 2, -3) == INVALID
+    assert _stats_status(lib, d, 0, 0, 20, -16) == INVALID
+    assert _stats_status(lib, d, 0, 0, -3, 7) == OK
+    assert _stats_status(lib, d, 0, 0, -3, 2) == INVALID
+    assert _stats_status(lib, d, 0, 0, -16, 20) == INVALID
+    assert _stats_status(lib, d, 0, 0, 2**63 - 1, 2**63 - 1) == OK
+    assert _stats_status(lib, d, 0, 0, -2**63, 5) == INVALID
+
+
+def test_mode4_must_intersect(lib):
+    d = bnsd(Sq=16, Skv=24)
+    assert _stats_status(lib, d, 0, 4, 3, -3) == OK
+    assert _stats_status(lib, d, 0, 4, 3, -4) == INVALID
+    assert _stats_status(lib, d, 0, 4, 1024, 0) == OK
+
+
+def test_mode7_mode8_rules_from_page_examples(lib):
+    """The worked examples of sparseMode=7 / 8 pass; moving pre or next past the stated
+    limits fails; both modes need the TND layout."""
+    q7, k7 = [3, 2], [3, 6]
+    cq, ck = synth.cumulative_ends(q7), synth.cumulative_ends(k7)
+    d7 = tnd(q7, k7)
+    assert _stats_status(lib, d7, 2, 7, 6, -2, cq, ck) == OK
+    assert _stats_status(lib, d7, 2, 7, 5, -2, cq, ck) == INVALID      # pre < last Skv
+    assert _stats_status(lib, d7, 2, 7, 6, 1, cq, ck) == INVALID       # next > 0
+    assert _stats_status(lib, d7, 2, 7, 6, -5, cq, ck) == INVALID      # next < last_Sq - last_Skv
+    assert _stats_status(lib, d7, 2, 7, 6, -4, cq, ck) == OK
+    # a non-band batch with Sq > Skv
+    qb, kb = [4, 2], [3, 6]
+    assert _stats_status(lib, tnd(qb, kb), 2, 7, 6, -2, synth.cumulative_ends(qb),
+                         synth.cumulative_ends(kb)) == INVALID
+    q8, k8 = [3, 5, 4], [4, 5, 4]
+    cq, ck = synth.cumulative_ends(q8), synth.cumulative_ends(k8)
+    d8 = tnd(q8, k8)
+    assert _stats_status(lib, d8, 2, 8, 4, 1, cq, ck) == OK
+    assert _stats_status(lib, d8, 2, 8, 3, 1, cq, ck) == INVALID       # pre < first Skv
+    assert _stats_status(lib, d8, 2, 8, 4, -2, cq, ck) == INVALID      # next < first_Sq - first_Skv
+    assert _stats_status(lib, d8, 2, 8, 4, -1, cq, ck) == OK
+    assert _stats_status(lib, bnsd(), 0, 7, 64, 0) == INVALID
+    assert _stats_status(lib, bnsd(), 1, 8, 64, 0) == INVALID
+
+
+def test_varlen_array_rules(lib):
+    d = tnd([3, 2], [3, 6])
+    assert _stats_status(lib, d, 2, 3, qlen=None, kvlen=[3, 9]) == NULLPTR
+    assert _stats_status(lib, d, 2, 3, qlen=[3, 5], kvlen=[3, 9]) == OK
+    assert _stats_status(lib, d, 2, 3, qlen=[3, 2], kvlen=[3, 9]) == INVALID   # not cumulative
+    assert _stats_status(lib, d, 2, 3, qlen=[3, 6], kvlen=[3, 9]) == INVALID   # T_q mismatch
+    assert _stats_status(lib, d, 2, 3, qlen=[-1, 5], kvlen=[3, 9]) == INVALID
+
+
+def test_prefix_and_mask_rules(lib):
+    d = bnsd()
+    assert _stats_status(lib, d, 0, 5) == NULLPTR
+    assert _stats_status(lib, d, 0, 5, prefix=[3, 9]) == OK
+    assert _stats_status(lib, d, 0, 6, prefix=[3, -1]) == INVALID
+    assert _stats_status(lib, d, 0, 1) == NULLPTR
+    assert _stats_status(lib, d, 0, 1, mask=True) == OK
+    assert _stats_status(lib, tnd([3], [3]), 2, 1, qlen=[3], kvlen=[3], mask=True) == UNSUPPORTED
+
+
+def test_fwd_rejects_before_device_work(lib):
+    """fa_fwd returns its status before touching the GPU: null data pointers, a too-small
+    workspace and invalid arguments come back without a HIP call (this host has no GPU)."""
+    buf = (ctypes.c_char * 4096)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    d = bnsd()
+    st = lib.fa_fwd(None, p, p, p, p, ctypes.byref(d), 0, 3, 0, 0, None, None, None, None, None, None,
+                    0.125, None, 0, None)
+    assert st == NULLPTR
+    d2 = tnd([3, 2], [3, 6])
+    need = fb.fa_fwd_workspace_size(d2, "TND", 3, [3, 5], [3, 9])
+    assert need > 0
+    st = lib.fa_fwd(p, p, p, p, p, ctypes.byref(d2), 2, 3, 0, 0, fb._i64([3, 5]), fb._i64([3, 9]), None,
+                    None, None, None, 0.125, p, need - 1, None)
+    assert st == WORKSPACE
+    st = lib.fa_fwd(p, p, p, p, p, ctypes.byref(d2), 2, 3, 0, 0, fb._i64([3, 5]), fb._i64([3, 9]), None,
+                    None, None, None, 0.125, None, 0, None)
+    assert st == NULLPTR
+    st = lib.fa_fwd(p, p, p, p, p, ctypes.byref(d), 0, 4, 3, -9, None, None, None, None, None, None,
+                    0.125, None, 0, None)
+    assert st == INVALID
+    # empty problem: nothing to do, OK without pointers
+    d0 = bnsd(B=0)
+    st = lib.fa_fwd(None, None, None, None, None, ctypes.byref(d0), 0, 3, 0, 0, None, None, None, None,
+                    None, None, 0.125, None, 0, None)
+    assert st == OK
+
+
+def test_workspace_size(lib):
+    assert fb.fa_fwd_workspace_size(bnsd(), "BNSD", 3) == 0
+    assert fb.fa_fwd_workspace_size(bnsd(), "BNSD", 5) > 0
+    d = tnd([300, 7], [300, 9])
+    n = fb.fa_fwd_workspace_size(d, "TND", 3, [300, 307], [300, 309])
+    bm, bn, nq, nk = fb.fa_tile_shape(d, "TND", [300, 307], [300, 309])
+    assert (bm, bn) == (128, 64)
+    assert nq == 3 + 1 and nk == 5
+    assert n >= 2 * 32 + nq * 8
+    d32 = tnd([300, 7], [300, 9], dtype=0, D=16)
+    bm, bn, nq, nk = fb.fa_tile_shape(d32, "TND", [300, 307], [300, 309])
+    assert (bm, bn) == (64, 16)
+
+
+# ---------------------------------------------------------------------------------------
+# Host tile planning vs brute force over the oracle's mask
+# ---------------------------------------------------------------------------------------
+
+def brute_tiles(vis, bm, bn):
+    """(visited, full) tile counts for one batch from an explicit visible matrix: a tile is
+    visited iff it holds a visible entry; full iff it lies inside the sequence and every
+    entry of its in-range rows is visible."""
+    sq, skv = vis.shape
+    visited = full = 0
+    for i0 in range(0, sq, bm):
+        for j0 in range(0, skv, bn):
+            blk = vis[i0:i0 + bm, j0:j0 + bn]
+            if blk.any():
+                visited += 1
+                if j0 + bn <= skv and blk.all():
+                    full += 1
+    return visited, full
+
+
+def _random_case(rng, mode):
+    sq = int(rng.integers(0, 300))
+    skv = int(rng.integers(0, 300))
+    if mode in (7,):
+        skv = max(skv, sq)
+    while True:
+        pre = int(rng.integers(-sq, sq + skv + 3))
+        nxt = int(rng.integers(-skv, sq + skv + 3))
+        if mode == 0:
+            if nxt < 0 and not (pre >= -nxt and -nxt < max(skv, 1)):
+                continue
+            if pre < 0 and not (nxt >= -pre and -pre < max(sq, 1)):
+                continue
+        if mode == 4 and pre + nxt < 0:
+            continue
+        return sq, skv, pre, nxt
+
+
+@pytest.mark.parametrize("mode", [0, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("dtype,D", [(2, 128), (0, 16)])
+def test_plan_tiles_match_brute_force(lib, mode, dtype, D):
+    rng = np.random.default_rng(500 + mode + 17 * dtype)
+    for _ in range(12):
+        sq, skv, pre, nxt = _random_case(rng, mode)
+        B = 2
+        prefix = [int(rng.integers(0, skv + 3)) for _ in range(B)]
+        d = bnsd(B=B, N=1, Sq=sq, Skv=skv, D=D, dtype=dtype)
+        st = fb.fa_plan_stats(d, "BNSD", mode, pre_tokens=pre, next_tokens=nxt, prefix=prefix, scale=0.1)
+        bm, bn = st["block_m"], st["block_n"]
+        vis_tot = full_tot = total = 0
+        for b in range(B):
+            vis = oracle.visible_matrix(mode, sq, skv, pre_tokens=pre, next_tokens=nxt, prefix_len=prefix[b])
+            v, f = brute_tiles(vis, bm, bn)
+            vis_tot += v
+            full_tot += f
+            total += -(-sq // bm) * -(-skv // bn)
+        assert st["kv_tiles_visited"] == vis_tot, (mode, sq, skv, pre, nxt, prefix)
+        assert st["kv_tiles_full"] == full_tot, (mode, sq, skv, pre, nxt, prefix)
+        assert st["kv_tiles_total"] == total
+
+
+@pytest.mark.parametrize("mode", [3, 7, 8])
+def test_plan_tiles_varlen_match_brute_force(lib, mode):
+    rng = np.random.default_rng(600 + mode)
+    for _ in range(10):
+        nb = int(rng.integers(1, 5))
+        ql = [int(x) for x in rng.integers(0, 260, nb)]
+        kl = [int(x) for x in rng.integers(0, 260, nb)]
+        if mode == 7:
+            kl = [max(a, b) for a, b in zip(ql, kl)]
+        band = oracle.band_batch_index(mode, ql, kl)
+        pre = nxt = 0
+        if band is not None:
+            sqb, skb = ql[band], kl[band]
+            pre = skb + int(rng.integers(0, 5))
+            if mode == 7:
+                nxt = int(rng.integers(sqb - skb, 1))
+            else:
+                nxt = sqb - skb + int(rng.integers(0, 5))
+        d = tnd(ql, kl, N=1)
+        cq, ck = synth.cumulative_ends(ql), synth.cumulative_ends(kl)
+        st = fb.fa_plan_stats(d, "TND", mode, pre_tokens=pre, next_tokens=nxt, actual_seq_qlen=cq,
+                              actual_seq_kvlen=ck, scale=0.1)
+        vt = ft = 0
+        for b in range(nb):
+            vis = oracle.visible_matrix(mode, ql[b], kl[b], pre_tokens=pre, next_tokens=nxt, band=(b == band))
+            v, f = brute_tiles(vis, st["block_m"], st["block_n"])
+            vt += v
+            ft += f
+        assert (st["kv_tiles_visited"], st["kv_tiles_full"]) == (vt, ft), (ql, kl, pre, nxt)

@@ -1,0 +1,453 @@
+"""GPU parity: libfa.so (through its C ABI) against the fp64 oracle on the same seeded inputs.
+
+Tolerances (against the fp64 oracle):
+  fp32 inputs:       max |dO| <= 1e-5, max |dLSE| <= 1e-5
+  fp16 / bf16:       |dO| <= 2e-2 + 1e-2 |O_ref| per element, |dLSE| <= 1e-3
+  fully masked rows: O == 0 and LSE == -inf exactly
+Mask / visible-pair counts and tile classes are integer work: compared bit-exactly.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from masked_attention_forward_amd import binding as fb
+from masked_attention_forward_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def to64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run(q, k, v, layout, mode, scale, dev, slopes=None, mask=None, **kw):
+    qd, kd, vd = (x.to(dev).contiguous() for x in (q, k, v))
+    sl = torch.tensor(slopes, dtype=torch.float32, device=dev) if slopes is not None else None
+    md = torch.from_numpy(np.ascontiguousarray(mask)).to(dev) if mask is not None else None
+    print(f"[case] layout={layout} mode={mode} q={tuple(q.shape)} k={tuple(k.shape)} dtype={q.dtype} "
+          f"alibi={slopes is not None} kw={ {a: b for a, b in kw.items() if not isinstance(b, list) or len(b) < 20} }",
+          flush=True)
+    o, lse = fb.flash_attention(qd, kd, vd, layout=layout, sparse_mode=mode, scale=scale,
+                                alibi_slopes=sl, atten_mask=md, **kw)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def check(o, lse, ref_o, ref_lse, dtype, what=""):
+    o = to64(o)
+    lse = lse.double().numpy()
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: empty-row pattern differs"
+    live = ~empty
+    if dtype == torch.float32:
+        err = np.abs(o - ref_o)
+        assert err.max(initial=0) <= 1e-5, f"{what}: max |dO| {err.max()}"
+        assert np.abs(lse[live] - ref_lse[live]).max(initial=0) <= 1e-5, what
+    else:
+        bound = 2e-2 + 1e-2 * np.abs(ref_o)
+        bad = np.abs(o - ref_o) > bound
+        assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max err {np.abs(o - ref_o).max()}"
+        assert np.abs(lse[live] - ref_lse[live]).max(initial=0) <= 1e-3, \
+            f"{what}: max |dLSE| {np.abs(lse[live] - ref_lse[live]).max()}"
+
+
+def zero_rows_ok(o, lse, layout):
+    """O rows whose LSE is -inf must be exactly zero."""
+    o = to64(o)
+    lse = lse.numpy()
+    if layout == "BNSD":
+        rows = o[np.isneginf(lse)]
+    elif layout == "BSND":
+        rows = o.transpose(0, 2, 1, 3)[np.isneginf(lse)]
+    else:
+        rows = o.transpose(1, 0, 2)[np.isneginf(lse)]
+    assert np.all(rows == 0.0)
+
+
+def make_inputs(layout, dtype, B, N, sq, skv, D, seed, qlens=None, kvlens=None):
+    w = synth.Workload("t", layout, dtype, B, N, D, sq, skv, qlens=qlens, kvlens=kvlens, seed=seed)
+    return w.tensors()
+
+
+# ---------------------------------------------------------------------------------------
+# Mask probe: device mask code vs the oracle's predicate, bit-exact.
+# ---------------------------------------------------------------------------------------
+
+def brute_class(vis, bm, bn, n_kv_max):
+    sq, skv = vis.shape
+    rows = []
+    for i0 in range(0, sq, bm):
+        r = []
+        for kt in range(n_kv_max):
+            j0 = kt * bn
+            if j0 >= skv:
+                r.append(3)
+                continue
+            blk = vis[i0:i0 + bm, j0:j0 + bn]
+            if not blk.any():
+                r.append(0)
+            elif j0 + bn <= skv and blk.all():
+                r.append(2)
+            else:
+                r.append(1)
+        rows.append(r)
+    return rows
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 16)])
+@pytest.mark.parametrize("mode", [0, 2, 3, 4, 5, 6])
+def test_probe_exact_bnsd(gpu_device, dtype, D, mode):
+    rng = np.random.default_rng(900 + mode)
+    for _ in range(6):
+        sq, skv = int(rng.integers(0, 400)), int(rng.integers(0, 400))
+        while True:
+            pre = int(rng.integers(-sq, sq + skv + 3))
+            nxt = int(rng.integers(-skv, sq + skv + 3))
+            if mode == 0 and ((nxt < 0 and not (pre >= -nxt and -nxt < max(skv, 1))) or
+                              (pre < 0 and not (nxt >= -pre and -pre < max(sq, 1)))):
+                continue
+            if mode == 4 and pre + nxt < 0:
+                continue
+            break
+        B, N = 2, 2
+        prefix = [int(rng.integers(0, skv + 2)) for _ in range(B)]
+        dims = fb.make_dims(DT[dtype], 0, B=B, N=N, Sq=sq, Skv=skv, D=D)
+        print(f"[probe] mode={mode} sq={sq} skv={skv} pre={pre} next={nxt} prefix={prefix}", flush=True)
+        counts, tiles = fb.fa_mask_probe(dims, "BNSD", mode, device=gpu_device, pre_tokens=pre,
+                                         next_tokens=nxt, prefix=prefix)
+        torch.cuda.synchronize()
+        counts = counts.cpu().numpy()
+        bm, bn, nq, nk = fb.fa_tile_shape(dims, "BNSD")
+        exp_tiles = []
+        for b in range(B):
+            vis = oracle.visible_matrix(mode, sq, skv, pre_tokens=pre, next_tokens=nxt, prefix_len=prefix[b])
+            for h in range(N):
+                assert counts[b, h].tolist() == vis.sum(axis=1).tolist()
+            exp_tiles += brute_class(vis, bm, bn, nk)
+        if nq and nk:
+            assert tiles.cpu().numpy().tolist() == exp_tiles
+
+
+@pytest.mark.parametrize("mode", [3, 7, 8])
+def test_probe_exact_tnd(gpu_device, mode):
+    rng = np.random.default_rng(950 + mode)
+    for _ in range(6):
+        nb = int(rng.integers(1, 6))
+        ql = [int(x) for x in rng.integers(0, 300, nb)]
+        kl = [int(x) for x in rng.integers(0, 300, nb)]
+        if mode == 7:
+            kl = [max(a, b) for a, b in zip(ql, kl)]
+        band = oracle.band_batch_index(mode, ql, kl)
+        pre = nxt = 0
+        if band is not None:
+            pre = kl[band] + int(rng.integers(0, 4))
+            nxt = int(rng.integers(ql[band] - kl[band], 1)) if mode == 7 else ql[band] - kl[band] + int(rng.integers(0, 4))
+        cq, ck = synth.cumulative_ends(ql), synth.cumulative_ends(kl)
+        dims = fb.make_dims(torch.bfloat16, 2, B=nb, N=2, D=128, T_q=sum(ql), T_kv=sum(kl))
+        print(f"[probe-tnd] mode={mode} ql={ql} kl={kl} pre={pre} next={nxt}", flush=True)
+        counts, tiles = fb.fa_mask_probe(dims, "TND", mode, device=gpu_device, pre_tokens=pre, next_tokens=nxt,
+                                         actual_seq_qlen=cq, actual_seq_kvlen=ck)
+        torch.cuda.synchronize()
+        counts = counts.cpu().numpy()
+        bm, bn, nq, nk = fb.fa_tile_shape(dims, "TND", cq, ck)
+        exp_tiles = []
+        start = 0
+        for b in range(nb):
+            vis = oracle.visible_matrix(mode, ql[b], kl[b], pre_tokens=pre, next_tokens=nxt, band=(b == band))
+            for h in range(2):
+                assert counts[h, start:start + ql[b]].tolist() == vis.sum(axis=1).tolist()
+            exp_tiles += brute_class(vis, bm, bn, nk)
+            start += ql[b]
+        if nq and nk:
+            assert tiles.cpu().numpy().tolist() == exp_tiles
+
+
+def test_probe_dense_mask_counts(gpu_device):
+    rng = np.random.default_rng(77)
+    B, N, sq, skv = 2, 3, 70, 133
+    for bc in ([0, 0], [1, 0], [0, 1], [1, 1]):
+        mb, mh = (1 if bc[0] else B), (1 if bc[1] else N)
+        mask = (rng.random((mb, mh, sq, skv)) < 0.6).astype(np.uint8)
+        dims = fb.make_dims(torch.bfloat16, 0, B=B, N=N, Sq=sq, Skv=skv, D=128)
+        counts, _ = fb.fa_mask_probe(dims, "BNSD", 1, device=gpu_device,
+                                     atten_mask=torch.from_numpy(mask).to(gpu_device), mask_bcast=bc)
+        counts = counts.cpu().numpy()
+        for b in range(B):
+            for h in range(N):
+                m = mask[0 if bc[0] else b, 0 if bc[1] else h]
+                assert counts[b, h].tolist() == (m == 0).sum(axis=1).tolist()
+
+
+# ---------------------------------------------------------------------------------------
+# Small-shape parity over modes, dtypes, layouts, head sizes (several tiles + ragged tails)
+# ---------------------------------------------------------------------------------------
+
+VARIANTS = [("bf16", 128, "BNSD"), ("f16", 128, "BSND"), ("bf16", 64, "BSND"), ("f16", 64, "BNSD"),
+            ("f32", 16, "BNSD"), ("f32", 128, "BSND"), ("bf16", 40, "BNSD")]
+
+MODE_ARGS = {
+    0: [dict(pre_tokens=synth.NO_MASK, next_tokens=synth.NO_MASK), dict(pre_tokens=9, next_tokens=-3),
+        dict(pre_tokens=-3, next_tokens=70), dict(pre_tokens=100, next_tokens=0), dict(pre_tokens=5, next_tokens=20)],
+    2: [{}], 3: [{}], 4: [dict(pre_tokens=60, next_tokens=0), dict(pre_tokens=30, next_tokens=-10)],
+    5: [dict(prefix=[0, 150])], 6: [dict(prefix=[77, 3])],
+}
+
+
+@pytest.mark.parametrize("mode", [0, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("alibi", [False, True])
+def test_parity_small(gpu_device, mode, alibi):
+    for vi, (dtype, D, layout) in enumerate(VARIANTS):
+        for (sq, skv) in [(300, 200), (130, 333)]:
+            for args in MODE_ARGS[mode]:
+                B, N = 2, 3
+                q, k, v = make_inputs(layout, dtype, B, N, sq, skv, D, seed=1000 * mode + 10 * vi + sq % 7)
+                if mode == 0 and args.get("next_tokens", 0) < 0 and -args["next_tokens"] >= skv:
+                    continue
+                if mode == 0 and args.get("pre_tokens", 0) < 0 and -args["pre_tokens"] >= sq:
+                    continue
+                slopes = synth.alibi_slopes(N) if alibi else None
+                scale = 1.0 / math.sqrt(D)
+                o, lse = run(q, k, v, layout, mode, scale, gpu_device, slopes=slopes, **args)
+                ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout=layout, sparse_mode=mode,
+                                                  scale=scale, alibi_slopes=slopes, **args)
+                check(o, lse, ref_o, ref_lse, DT[dtype], f"mode={mode} {dtype} D={D} {layout} {sq}x{skv} {args}")
+                zero_rows_ok(o, lse, layout)
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_parity_dense_mask(gpu_device, alibi):
+    rng = np.random.default_rng(31)
+    for dtype, D, layout in VARIANTS[:5]:
+        B, N, sq, skv = 2, 3, 150, 170
+        q, k, v = make_inputs(layout, dtype, B, N, sq, skv, D, seed=55)
+        for bc in ([0, 0], [1, 1], [1, 0]):
+            mb, mh = (1 if bc[0] else B), (1 if bc[1] else N)
+            mask = (rng.random((mb, mh, sq, skv)) < 0.7).astype(np.uint8)
+            mask[..., 5, :] = 1     # a fully masked row
+            slopes = synth.alibi_slopes(N) if alibi else None
+            o, lse = run(q, k, v, layout, 1, 0.1, gpu_device, slopes=slopes, mask=mask, mask_bcast=bc)
+            ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout=layout, sparse_mode=1, scale=0.1,
+                                              atten_mask=mask, alibi_slopes=slopes)
+            check(o, lse, ref_o, ref_lse, DT[dtype], f"mode=1 {dtype} {layout} bcast={bc}")
+            zero_rows_ok(o, lse, layout)
+
+
+@pytest.mark.parametrize("mode", [3, 5, 7, 8])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64), ("f32", 32)])
+def test_parity_tnd(gpu_device, mode, dtype, D):
+    rng = np.random.default_rng(4000 + mode)
+    ql = [200, 0, 1, 129, 64, 257]
+    kl = [150, 5, 0, 300, 64, 257]
+    if mode == 7:
+        kl = [max(a, b) for a, b in zip(ql, kl)]
+    band = oracle.band_batch_index(mode, ql, kl)
+    kw = {}
+    if mode == 7:
+        kw = dict(pre_tokens=kl[band], next_tokens=ql[band] - kl[band])
+    if mode == 8:
+        kw = dict(pre_tokens=kl[band] + 3, next_tokens=ql[band] - kl[band] + 2)
+    if mode == 5:
+        kw = dict(prefix=[int(x) for x in rng.integers(0, 320, len(ql))])
+    N = 4
+    q, k, v = make_inputs("TND", dtype, len(ql), N, 0, 0, D, seed=77 + mode, qlens=ql, kvlens=kl)
+    cq, ck = synth.cumulative_ends(ql), synth.cumulative_ends(kl)
+    slopes = synth.alibi_slopes(N) if mode in (3, 5) else None
+    o, lse = run(q, k, v, "TND", mode, 0.09, gpu_device, slopes=slopes, actual_seq_qlen=cq, actual_seq_kvlen=ck, **kw)
+    ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout="TND", sparse_mode=mode, scale=0.09,
+                                      actual_seq_qlen=cq, actual_seq_kvlen=ck, alibi_slopes=slopes, **kw)
+    check(o, lse, ref_o, ref_lse, DT[dtype], f"TND mode={mode} {dtype}")
+    zero_rows_ok(o, lse, "TND")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_causal"])
+def test_page_example_tiny_f32(gpu_device, name):
+    """Exercise page example 1 (seed 42, (2,12,16)) as fp32 BNSD with one head: no mask and
+    the causal variant pre=12, next=0; max |dO| <= 1e-5 against the fp64 oracle."""
+    w = synth.workloads()[name]
+    q, k, v = w.tensors()
+    o, lse = run(q, k, v, "BNSD", w.sparse_mode, w.softmax_scale, gpu_device, pre_tokens=w.pre_tokens,
+                 next_tokens=w.next_tokens)
+    ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout="BNSD", sparse_mode=w.sparse_mode,
+                                      scale=w.softmax_scale, pre_tokens=w.pre_tokens, next_tokens=w.next_tokens)
+    check(o, lse, ref_o, ref_lse, torch.float32, name)
+
+
+def test_band_negative_next_16(gpu_device):
+    """sparseMode=0, preTokens=9, nextTokens=-3 at Sq=Skv=16, D=128 bf16: full comparison,
+    rows 0-2 fully masked."""
+    w = synth.workloads()["band_neg_16"]
+    q, k, v = w.tensors()
+    o, lse = run(q, k, v, "BNSD", 0, w.softmax_scale, gpu_device, pre_tokens=9, next_tokens=-3)
+    ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout="BNSD", sparse_mode=0,
+                                      scale=w.softmax_scale, pre_tokens=9, next_tokens=-3)
+    check(o, lse, ref_o, ref_lse, torch.bfloat16, "band_neg_16")
+    assert np.all(np.isneginf(lse.numpy()[0, 0, :3]))
+    assert np.all(to64(o)[0, 0, :3] == 0)
+
+
+# ---------------------------------------------------------------------------------------
+# Query split (sparseMode 7 / 8) reproduces the unsplit rows
+# ---------------------------------------------------------------------------------------
+
+def _split_compare(dev, unsplit, shards, N, D, dtype, seed):
+    """unsplit = (mode, qlens, kvlens, kw); shards = [(mode, [(ub, r0, n)], kw)]."""
+    mode_u, qlens, kvlens, kw_u = unsplit
+    g = torch.Generator().manual_seed(seed)
+    qs = [torch.randn(n, N, D, generator=g).to(DT[dtype]) for n in qlens]
+    ks = [torch.randn(n, N, D, generator=g).to(DT[dtype]) for n in kvlens]
+    vs = [torch.randn(n, N, D, generator=g).to(DT[dtype]) for n in kvlens]
+    cq, ck = synth.cumulative_ends(qlens), synth.cumulative_ends(kvlens)
+    o_u, l_u = run(torch.cat(qs), torch.cat(ks), torch.cat(vs), "TND", mode_u, 0.088, dev,
+                   actual_seq_qlen=cq, actual_seq_kvlen=ck, **kw_u)
+    starts = [0] + cq[:-1]
+    for mode_s, parts, kw in shards:
+        q = torch.cat([qs[ub][r0:r0 + n] for ub, r0, n in parts])
+        k = torch.cat([ks[ub] for ub, _, _ in parts])
+        v = torch.cat([vs[ub] for ub, _, _ in parts])
+        sq = synth.cumulative_ends([n for _, _, n in parts])
+        sk = synth.cumulative_ends([kvlens[ub] for ub, _, _ in parts])
+        o_s, l_s = run(q, k, v, "TND", mode_s, 0.088, dev, actual_seq_qlen=sq, actual_seq_kvlen=sk, **kw)
+        row = 0
+        for ub, r0, n in parts:
+            src = starts[ub] + r0
+            assert torch.equal(o_s[row:row + n], o_u[src:src + n]), (mode_s, ub, r0, n)
+            assert torch.equal(l_s[:, row:row + n], l_u[:, src:src + n]), (mode_s, ub, r0, n)
+            row += n
+
+
+def test_split_page_examples_gpu(gpu_device):
+    """The sparseMode=7 and =8 worked examples on the GPU: shards == unsplit, bitwise."""
+    _split_compare(gpu_device, (3, [3, 4, 5, 4], [3, 6, 5, 4], {}),
+                   [(7, [(0, 0, 3), (1, 0, 2)], dict(pre_tokens=6, next_tokens=-2)),
+                    (3, [(1, 2, 2), (2, 0, 5), (3, 0, 4)], {})], N=2, D=128, dtype="bf16", seed=7)
+    _split_compare(gpu_device, (2, [3, 5, 5, 4], [3, 4, 5, 4], {}),
+                   [(2, [(0, 0, 3), (1, 0, 2)], {}),
+                    (8, [(1, 2, 3), (2, 0, 5), (3, 0, 4)], dict(pre_tokens=4, next_tokens=1))],
+                   N=2, D=128, dtype="bf16", seed=8)
+
+
+def test_split_varlen_config(gpu_device):
+    """Varlen TND config (16 lengths U[128, 4096], N=32, D=128, bf16): the last sequence's
+    queries cut in two (mode 7 band shard + mode 3 shard) give the unsplit mode-3 rows; the
+    mirror cut of the first sequence (mode 2 shard + mode 8 band shard) gives the unsplit
+    mode-2 rows."""
+    w = synth.workloads()["varlen_tnd"]
+    L = w.qlens
+    last = len(L) - 1
+    q1 = L[last] // 2
+    shard_a = [(b, 0, L[b]) for b in range(last)] + [(last, 0, q1)]
+    _split_compare(gpu_device, (3, L, L, {}),
+                   [(7, shard_a, dict(pre_tokens=L[last], next_tokens=q1 - L[last])),
+                    (3, [(last, q1, L[last] - q1)], {})], N=32, D=128, dtype="bf16", seed=4)
+    q0 = L[0] // 2
+    shard_2 = [(0, q0, L[0] - q0)] + [(b, 0, L[b]) for b in range(1, len(L))]
+    _split_compare(gpu_device, (2, L, L, {}),
+                   [(2, [(0, 0, q0)], {}),
+                    (8, shard_2, dict(pre_tokens=L[0], next_tokens=0))],
+                   N=32, D=128, dtype="bf16", seed=5)
+
+
+# ---------------------------------------------------------------------------------------
+# Full-size configs: sampled rows against the oracle
+# ---------------------------------------------------------------------------------------
+
+def _sample_rows(w, rng, n_random=24):
+    rows = []
+    if w.layout == "TND":
+        bs = [0, len(w.qlens) // 2, len(w.qlens) - 1]
+        for b in bs:
+            L = w.qlens[b]
+            for h in (0, w.N - 1):
+                for i in {0, 1, min(127, L - 1), min(128, L - 1), L // 2, L - 1}:
+                    rows.append((b, h, i))
+        for _ in range(n_random):
+            b = int(rng.integers(0, len(w.qlens)))
+            rows.append((b, int(rng.integers(0, w.N)), int(rng.integers(0, w.qlens[b]))))
+        return rows
+    for b in {0, w.B - 1}:
+        for h in {0, w.N // 2, w.N - 1}:
+            for i in {0, 1, 127, 128, 255, 256, 257, w.Sq // 2, w.Sq - 2, w.Sq - 1}:
+                rows.append((b, h, i))
+    for _ in range(n_random):
+        rows.append((int(rng.integers(0, w.B)), int(rng.integers(0, w.N)), int(rng.integers(0, w.Sq))))
+    return rows
+
+
+def _gather(o, lse, w, rows):
+    o = to64(o) if not isinstance(o, np.ndarray) else o
+    lse = lse.double().numpy()
+    out_o, out_l = [], []
+    starts = [0] + (w.actual_seq_qlen[:-1] if w.layout == "TND" else [])
+    for b, h, i in rows:
+        if w.layout == "BNSD":
+            out_o.append(o[b, h, i]); out_l.append(lse[b, h, i])
+        elif w.layout == "BSND":
+            out_o.append(o[b, i, h]); out_l.append(lse[b, h, i])
+        else:
+            out_o.append(o[starts[b] + i, h]); out_l.append(lse[h, starts[b] + i])
+    return np.array(out_o), np.array(out_l)
+
+
+@pytest.mark.parametrize("name", ["causal_2048", "band_8192", "band_neg_8192", "causal_8192",
+                                  "varlen_tnd", "prefix_alibi", "prefix_alibi_square"])
+def test_config_sampled_rows(gpu_device, name):
+    w = synth.workloads()[name]
+    q, k, v = w.tensors()
+    kw = dict(pre_tokens=w.pre_tokens, next_tokens=w.next_tokens, prefix=w.prefix,
+              actual_seq_qlen=w.actual_seq_qlen, actual_seq_kvlen=w.actual_seq_kvlen)
+    o, lse = run(q, k, v, w.layout, w.sparse_mode, w.softmax_scale, gpu_device, slopes=w.slopes(), **kw)
+    rng = np.random.default_rng(hash(name) % 2**32)
+    rows = _sample_rows(w, rng)
+    qn, kn, vn = (x.float().numpy() for x in (q, k, v))
+    ref_o, ref_l = oracle.attention_rows(qn, kn, vn, rows, layout=w.layout, sparse_mode=w.sparse_mode,
+                                         scale=w.softmax_scale, alibi_slopes=w.slopes(), **kw)
+    got_o, got_l = _gather(o, lse, w, rows)
+    check(torch.from_numpy(got_o), torch.from_numpy(got_l), ref_o, ref_l, DT[w.dtype], name)
+    # every row: finite output, LSE finite or -inf
+    assert torch.isfinite(o).all()
+    assert not torch.isnan(lse).any()
+
+
+def test_deterministic(gpu_device):
+    w = synth.workloads()["causal_2048"]
+    q, k, v = w.tensors()
+    a = run(q, k, v, "BNSD", 3, w.softmax_scale, gpu_device)
+    b = run(q, k, v, "BNSD", 3, w.softmax_scale, gpu_device)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------------------
+# Empty and degenerate inputs
+# ---------------------------------------------------------------------------------------
+
+def test_empty_inputs(gpu_device):
+    dev = gpu_device
+    for dtype in ("bf16", "f32"):
+        for (B, sq, skv) in [(0, 5, 5), (2, 0, 7), (2, 7, 0), (1, 1, 1)]:
+            q, k, v = make_inputs("BNSD", dtype, B, 2, sq, skv, 128, seed=3)
+            o, lse = run(q, k, v, "BNSD", 3 if skv >= sq else 2, 0.1, dev)
+            ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout="BNSD",
+                                              sparse_mode=3 if skv >= sq else 2, scale=0.1)
+            assert o.shape == q.shape and lse.shape == (B, 2, sq)
+            if o.numel():
+                check(o, lse, ref_o, ref_lse, DT[dtype], f"empty {B} {sq} {skv}")
+    # TND with zero-length sequences and an empty total
+    q, k, v = make_inputs("TND", "bf16", 3, 2, 0, 0, 128, seed=4, qlens=[0, 0, 0], kvlens=[0, 4, 0])
+    o, lse = run(q, k, v, "TND", 3, 0.1, dev, actual_seq_qlen=[0, 0, 0], actual_seq_kvlen=[0, 4, 4])
+    assert o.numel() == 0 and lse.shape == (2, 0)
+
+
+def test_single_key_rows_return_value(gpu_device):
+    """sparseMode=0 with pre=next=0 leaves only the diagonal: O_i = v_i (to bf16 rounding of
+    P = 1, exact) and LSE_i = scale q_i.k_i."""
+    q, k, v = make_inputs("BNSD", "bf16", 1, 2, 200, 200, 128, seed=9)
+    o, lse = run(q, k, v, "BNSD", 0, 0.1, gpu_device, pre_tokens=0, next_tokens=0)
+    assert torch.equal(o, v)
+    ref = 0.1 * (to64(q) * to64(k)).sum(-1)
+    assert np.abs(lse.double().numpy() - ref).max() < 1e-4
