@@ -1,0 +1,199 @@
+"""Benchmark: masked attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one fa_fwd call over the whole workload (inputs already resident in HBM). The
+metric is effective TFLOP/s: 4 * D flops per visible (query, key) pair, summed over batches
+and heads, divided by the step time; masked or skipped work is never counted. The visible
+pair count comes from the library's mask probe (checked bit-exactly against the oracle by
+the test suite) and is cross-checked against a closed form where one exists.
+
+Prints one JSON line. Timing uses HIP events recorded on the stream fa_fwd is launched on
+(torch's current stream). The CPU baseline times the fp64 oracle on a bounded sample of
+the same workload (a few whole heads) on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["masked_attention_forward_amd/csrc/fa_kernels.hip",
+                  "masked_attention_forward_amd/csrc/fa_mask.h"]
+METRIC = "effective TFLOP/s (unmasked FLOPs) attn fwd bf16 D=128; % of MFMA peak"
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_mfma_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def visible_pairs(w, dev) -> int:
+    import torch
+    from masked_attention_forward_amd import binding as fb
+
+    from masked_attention_forward_amd import synth
+
+    qk = w.shapes()
+    q = torch.empty(qk[0], dtype=synth.DTYPES[w.dtype], device="meta")
+    k = torch.empty(qk[1], dtype=synth.DTYPES[w.dtype], device="meta")
+    dims = fb.dims_of(q, k, w.layout, w.actual_seq_qlen)
+    counts, _ = fb.fa_mask_probe(dims, w.layout, w.sparse_mode, device=dev, pre_tokens=w.pre_tokens,
+                                 next_tokens=w.next_tokens, actual_seq_qlen=w.actual_seq_qlen,
+                                 actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix, tiles=False)
+    total = int(counts.sum().item())
+    if w.sparse_mode == 3 and w.layout != "TND" and w.Sq <= w.Skv:
+        per_head = w.Sq * (w.Skv - w.Sq) + w.Sq * (w.Sq + 1) // 2
+        assert total == per_head * w.B * w.N, (total, per_head)
+    return total
+
+
+def cpu_baseline(w, heads: int):
+    """Time the fp64 oracle on `heads` whole (batch, head) slices of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q, k, v = w.tensors()
+    assert w.layout == "BNSD"
+    sel = [(b, h) for b in range(w.B) for h in range(w.N)][:heads]
+    flops = 0
+    t_total = 0.0
+    for b, h in sel:
+        qs = q[b:b + 1, h:h + 1].double().numpy()
+        ks = k[b:b + 1, h:h + 1].double().numpy()
+        vs = v[b:b + 1, h:h + 1].double().numpy()
+        slopes = [w.slopes()[h]] if w.alibi else None
+        prefix = [w.prefix[b]] if w.prefix is not None else None
+        t0 = time.perf_counter()
+        _, lse = oracle.attention(qs, ks, vs, layout="BNSD", sparse_mode=w.sparse_mode,
+                                  scale=w.softmax_scale, pre_tokens=w.pre_tokens,
+                                  next_tokens=w.next_tokens, prefix=prefix, alibi_slopes=slopes)
+        t_total += time.perf_counter() - t0
+        vis = oracle.visible_matrix(w.sparse_mode, w.Sq, w.Skv, pre_tokens=w.pre_tokens,
+                                    next_tokens=w.next_tokens,
+                                    prefix_len=prefix[0] if prefix else 0)
+        flops += 4 * w.D * int(vis.sum())
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(sel)} of {w.B * w.N} (batch, head) slices at full Sq={w.Sq}, Skv={w.Skv}; "
+                      f"{t_total:.1f} s of fp64 numpy (BLAS threads={threads}, elementwise on 1 core)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal_8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from masked_attention_forward_amd import binding as fb
+    from masked_attention_forward_amd import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.workloads()[args.workload]
+    q, k, v = (x.to(dev) for x in w.tensors())
+    slopes = torch.tensor(w.slopes(), dtype=torch.float32, device=dev) if w.alibi else None
+    out = torch.empty_like(q)
+    lse = torch.empty(fb.lse_shape(q, w.layout), dtype=torch.float32, device=dev)
+    dims = fb.dims_of(q, k, w.layout, w.actual_seq_qlen)
+    ws_bytes = fb.fa_fwd_workspace_size(dims, w.layout, w.sparse_mode, w.actual_seq_qlen, w.actual_seq_kvlen)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    kw = dict(layout=w.layout, sparse_mode=w.sparse_mode, pre_tokens=w.pre_tokens, next_tokens=w.next_tokens,
+              actual_seq_qlen=w.actual_seq_qlen, actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix,
+              alibi_slopes=slopes, scale=w.softmax_scale, workspace=ws if ws_bytes else None)
+    pairs = visible_pairs(w, dev)
+    flops = 4 * w.D * pairs
+    elem = q.element_size()
+    rows_q = q.numel() // w.D
+    rows_kv = k.numel() // w.D
+    alg_bytes = (2 * rows_q * w.D + 2 * rows_kv * w.D) * elem + 4 * rows_q
+
+    for _ in range(args.warmup):
+        fb.fa_fwd(q, k, v, out, lse, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fb.fa_fwd(q, k, v, out, lse, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = recorded_traffic(args.workload)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f16": "f16", "f32": "f32"}[w.dtype],
+        "data": "synthetic (seeded N(0,1) q/k/v)",
+        "config": {"workload": args.workload, "layout": w.layout, "sparse_mode": w.sparse_mode,
+                   "B": w.B, "N": w.N, "Sq": w.Sq, "Skv": w.Skv, "D": w.D,
+                   "pre_tokens": w.pre_tokens, "next_tokens": w.next_tokens,
+                   "alibi": w.alibi, "visible_pairs": pairs, "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes": alg_bytes,
+                     "kernel_sources_sha256": kernel_sources_sha()},
+    }
+    if not args.no_cpu_baseline and w.layout == "BNSD":
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

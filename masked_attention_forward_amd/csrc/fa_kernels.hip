@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -69,25 +70,39 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // Work item of this workgroup: heads are the fastest index, so the blocks of one (batch, head)
 // always land on the same XCD when N is a multiple of 8 (blocks go round-robin over XCDs);
 // items run heaviest first (the planner sorted the table, or reverse_qt flips the q tiles).
+// Values read from the workspace tables are the same for every lane; readfirstlane keeps them
+// in scalar registers (buffer descriptors built from them must be wave-uniform).
+__device__ __forceinline__ int fa_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ fa_geom fa_geom_of(const fa_kargs& a, int b) {
+    if (!a.geoms) return a.geom0;
+    const fa_geom t = a.geoms[b];
+    fa_geom g;
+    g.q_start = fa_uniform(t.q_start);
+    g.kv_start = fa_uniform(t.kv_start);
+    g.sq = fa_uniform(t.sq);
+    g.skv = fa_uniform(t.skv);
+    g.a = fa_uniform(t.a);
+    g.c = fa_uniform(t.c);
+    g.f = fa_uniform(t.f);
+    g.pad = 0;
+    return g;
+}
+
 __device__ __forceinline__ void fa_decode_item(const fa_kargs& a, int& b, int& h, int& qt,
                                                fa_geom& g) {
     const int w = blockIdx.x;
     h = w % a.N;
     const int item = w / a.N;
     if (a.items) {
-        b = a.items[2 * item];
-        qt = a.items[2 * item + 1];
-        g = a.geoms[b];
+        b = fa_uniform(a.items[2 * item]);
+        qt = fa_uniform(a.items[2 * item + 1]);
     } else {
         const int r = item / a.B;
         b = item % a.B;
         qt = a.reverse_qt ? a.n_qtiles_fixed - 1 - r : r;
-        g = a.geom0;
     }
-}
-
-__device__ __forceinline__ fa_geom fa_geom_of(const fa_kargs& a, int b) {
-    return a.geoms ? a.geoms[b] : a.geom0;
+    g = fa_geom_of(a, b);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -133,25 +148,64 @@ __device__ __forceinline__ int lds_idx8(int r, int c) {
     return line * 16 + ((8 * (r & 1) + c) ^ (line & 7));
 }
 
-constexpr int MF_BM = FA_MFMA_BM;   // 128 query rows per workgroup
-constexpr int MF_BN = FA_MFMA_BN;   // 64 keys per tile
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fa_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 fa_bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// max / sum of x over the lane pair (l, l ^ 32); both lanes get the same bits.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// K and V tiles live in LDS row-major (one row = D keys' worth of 16-byte chunks); chunk c of
+// row j sits at c ^ swz(j). For D = 128 the XOR spreads the 16 rows a 16-lane group reads
+// (ds_read_b128 of K) and the 4 rows x 32 bytes a transpose read of V touches over distinct
+// banks.
+template <int KCH>
+__device__ __forceinline__ int fa_swz(int j, int c) {
+    if constexpr (KCH == 16) return c ^ (((j & 7) << 1) | ((j >> 3) & 1));
+    else return c ^ ((j >> 1) & 7);
+}
+
+constexpr int MF_BM = FA_MFMA32_BM;   // 128 query rows per workgroup (4 waves x 32 rows)
+constexpr int MF_BN = FA_MFMA32_BN;   // 64 keys per kv tile
 constexpr int MF_THREADS = 256;
 
+// 32 query rows per wave, two workgroups per CU (two waves per SIMD, which take turns on the
+// matrix core and the VALU). K and V tiles go from HBM straight into LDS with buffer loads
+// (no register staging; rows past the last needed key read as zero), double-buffered and
+// prefetched one tile ahead. S^T = K Q^T puts one query row in each lane; P comes straight
+// from the S^T accumulators; the V^T operand of O^T += V^T P^T is read from the row-major V
+// tile with ds_read_b64_tr_b16 (lane i of each 16-lane group receives element i%4 of the
+// chunks addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4), so no transpose pass is needed.
 template <int D, bool IS_BF16, bool ALIBI, bool DENSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(MF_THREADS, MF_THREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 fa_fwd_mfma(const fa_kargs a) {
     static_assert(D == 64 || D == 128, "MFMA path covers D = 64 and 128");
     using io = mfma_io<IS_BF16>;
-    constexpr int KCH = D / 8;                       // 16-byte chunks per K row
-    constexpr int KSTEPS = D / 16;                   // k-steps of S^T = K Q^T
-    constexpr int DBLK = D / 32;                     // 32-row blocks of O^T
-    constexpr int KLOADS = MF_BN * KCH / MF_THREADS; // 16-byte K loads per thread
-    constexpr int VUNITS = (MF_BN / 4) * KCH;        // (4 keys x 8 d) V units per tile
-    static_assert(KLOADS >= 1 && VUNITS <= MF_THREADS, "tile shape");
+    constexpr int BM = MF_BM, BN = MF_BN, NT = MF_THREADS;
+    constexpr int KCH = D / 8;                   // 16-byte chunks per K / V row
+    constexpr int KSTEPS = D / 16;               // k-steps of S^T = K Q^T
+    constexpr int DBLK = D / 32;                 // 32-row blocks of O^T
+    constexpr int TILE_CHUNKS = BN * KCH;        // 16-byte chunks per K or V tile
+    constexpr int LOADS = TILE_CHUNKS / NT;      // direct loads per thread and tile
+    static_assert(LOADS >= 1 && TILE_CHUNKS % NT == 0, "tile shape");
 
-    __shared__ u32x4 lds_k[2][MF_BN * KCH];
-    __shared__ u32x4 lds_v[2][D * (MF_BN / 8)];
+    __shared__ u32x4 lds_k[2][TILE_CHUNKS];
+    __shared__ u32x4 lds_v[2][TILE_CHUNKS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -162,28 +216,34 @@ fa_fwd_mfma(const fa_kargs a) {
     int b, h, qt;
     fa_geom g;
     fa_decode_item(a, b, h, qt, g);
-    const int i0 = qt * MF_BM;
-    const int i_last = min(i0 + MF_BM, g.sq) - 1;
-    const fa_kv_range kr = fa_tile_kv_range(g, i0, i_last, MF_BN);
+    const int i0 = qt * BM;
+    const int i_last = min(i0 + BM, g.sq) - 1;
+    const fa_kv_range kr = fa_tile_kv_range(g, i0, i_last, BN);
+    const int n_tiles = kr.end - kr.begin;
+    const int kv_lim = min(kr.end * BN, g.skv);   // keys past this are never needed
 
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + h * a.q_hs +
-                         int64_t(g.q_start) * a.q_rs;
+                         (int64_t(g.q_start) + i0) * a.q_rs;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.kv_bs + h * a.kv_hs +
                          int64_t(g.kv_start) * a.kv_rs;
     const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.kv_bs + h * a.kv_hs +
                          int64_t(g.kv_start) * a.kv_rs;
+    const int q_rs = int(a.q_rs), kv_rs = int(a.kv_rs);
 
     // This lane's query row; Q^T is the B operand: lane holds d = 16 t + 8 hl .. + 7.
-    const int row = i0 + wave * 32 + ln;
+    const int lrow = wave * 32 + ln;
+    const int row = i0 + lrow;
     const bool row_ok = row < g.sq;
     u32x4 qop[KSTEPS];
+    {
+        const __amdgpu_buffer_rsrc_t rq = fa_rsrc(qp, ((min(g.sq - i0, BM) - 1) * q_rs + D) * 2);
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-        qop[t] = row_ok ? *reinterpret_cast<const u32x4*>(qp + int64_t(row) * a.q_rs + 16 * t + 8 * hl)
-                        : u32x4{0, 0, 0, 0};
+        for (int t = 0; t < KSTEPS; ++t) qop[t] = fa_bload(rq, (lrow * q_rs + 16 * t + 8 * hl) * 2);
     }
     const int row_lo = fa_row_lo(g, row);
     const int row_hi = fa_row_hi(g, row);
+    const int wrow0 = i0 + wave * 32;
+    const int wlast = min(wrow0 + 31, g.sq - 1);   // last valid row of this wave
     const float sl2 = a.scale_log2;
     float slope2 = 0.f;
     if (ALIBI) slope2 = a.slopes[h] * kLog2e;
@@ -197,84 +257,71 @@ fa_fwd_mfma(const fa_kargs a) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
 
-    u32x4 kreg[KLOADS];
-    u32x4 vreg[4];
-
-    auto gload = [&](int kt) {
-        const int j0 = kt * MF_BN;
+    // HBM -> LDS for one K or V tile: lane l of the wave's p-th load fills physical chunk
+    // P = 64 (LOADS wave + p) + l, i.e. row P / KCH, so it fetches that row's logical chunk.
+    auto dload = [&](const uint16_t* base, int kt, u32x4* dst) {
+        const int j0 = kt * BN;
+        const int rows = min(BN, kv_lim - j0);
+        const __amdgpu_buffer_rsrc_t r =
+            fa_rsrc(base + int64_t(j0) * kv_rs, rows > 0 ? ((rows - 1) * kv_rs + D) * 2 : 0);
 #pragma unroll
-        for (int p = 0; p < KLOADS; ++p) {
-            const int ci = p * MF_THREADS + tid;
-            const int r = ci / KCH, c = ci % KCH;
-            const int j = j0 + r;
-            kreg[p] = j < g.skv ? *reinterpret_cast<const u32x4*>(kp + int64_t(j) * a.kv_rs + c * 8)
-                                : u32x4{0, 0, 0, 0};
-        }
-        if (tid < VUNITS) {
-            const int dc = tid % KCH, jq = tid / KCH;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int j = j0 + 4 * jq + q;
-                vreg[q] = j < g.skv ? *reinterpret_cast<const u32x4*>(vp + int64_t(j) * a.kv_rs + dc * 8)
-                                    : u32x4{0, 0, 0, 0};
-            }
+        for (int p = 0; p < LOADS; ++p) {
+            const int blk = wave * LOADS + p;
+            const int P = blk * 64 + lane;
+            const int j = P / KCH;
+            const int c = fa_swz<KCH>(j, P % KCH);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + blk * 64), 16,
+                                                     (j * kv_rs + c * 8) * 2, 0, 0, 0);
         }
     };
 
-    // K rows as loaded (swizzled); V transposed to V^T[d][key position], where the key order
-    // inside each group of 16 swaps bits 2 and 3 so that the 8 keys one lane needs for a
-    // PV k-step sit in one 16-byte chunk.
-    auto sstore = [&](int buf) {
+    // Per-lane LDS byte offsets of the V^T operand halves (see the transpose-read note above):
+    // group lanes address rows 16 t + 8 h2 + 4 hl + (lane%16)/4 and columns
+    // 32 db + 16 ((lane/16)%2) + 4 (lane%4).
+    const int src = lane & 15;
+    const int dlo = 16 * ((lane >> 4) & 1) + 4 * (src & 3);
+    int v_off[2][DBLK];
 #pragma unroll
-        for (int p = 0; p < KLOADS; ++p) {
-            const int ci = p * MF_THREADS + tid;
-            const int r = ci / KCH, c = ci % KCH;
-            lds_k[buf][KCH == 16 ? lds_idx16(r, c) : lds_idx8(r, c)] = kreg[p];
-        }
-        if (tid < VUNITS) {
-            const int dc = tid % KCH, jq = tid / KCH;
-            const int jm = jq & 3;
-            const int jpos = 16 * (jq >> 2) + 8 * (jm & 1) + 4 * (jm >> 1);
-            const int cc = jpos >> 3, half = (jpos >> 2) & 1;
-            u32x2* vv = reinterpret_cast<u32x2*>(lds_v[buf]);
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int j = 8 * h2 + 4 * hl + (src >> 2);   // + 16 t
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
-                const u32x2 ev = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-                const u32x2 od = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-                const int d = 8 * dc + 2 * w;
-                vv[2 * lds_idx8(d, cc) + half] = ev;
-                vv[2 * lds_idx8(d + 1, cc) + half] = od;
-            }
+        for (int db = 0; db < DBLK; ++db) {
+            const int d0 = 32 * db + dlo;
+            v_off[h2][db] = (j * KCH + fa_swz<KCH>(j, d0 >> 3)) * 16 + (d0 & 7) * 2;
         }
-    };
+    }
+    int k_off[KSTEPS];
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) k_off[t] = ln * KCH + fa_swz<KCH>(ln, 2 * t + hl);   // + 32 jb rows
 
-    if (kr.begin < kr.end) {
-        gload(kr.begin);
-        sstore(0);
+    if (n_tiles > 0) {
+        dload(kp, kr.begin, lds_k[0]);
+        dload(vp, kr.begin, lds_v[0]);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        for (int kt = kr.begin; kt < kr.end; ++kt) {
-            const int buf = (kt - kr.begin) & 1;
-            const bool has_next = kt + 1 < kr.end;
-            if (has_next) gload(kt + 1);
-
+        for (int it = 0; it < n_tiles; ++it) {
+            const int buf = it & 1;
+            const int kt = kr.begin + it;
+            if (it + 1 < n_tiles) {
+                dload(kp, kt + 1, lds_k[buf ^ 1]);
+                dload(vp, kt + 1, lds_v[buf ^ 1]);
+            }
             // S^T (keys x rows): lane holds row `row`, keys j0 + 32 jb + 8 (r/4) + 4 hl + r%4.
             f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
             for (int t = 0; t < KSTEPS; ++t) {
 #pragma unroll
                 for (int jb = 0; jb < 2; ++jb) {
-                    const int r = 32 * jb + ln;
-                    const u32x4 kop = lds_k[buf][KCH == 16 ? lds_idx16(r, 2 * t + hl) : lds_idx8(r, 2 * t + hl)];
+                    const u32x4 kop = lds_k[buf][k_off[t] + 32 * jb * KCH];
                     sacc[jb] = io::mma(kop, qop[t], sacc[jb]);
                 }
             }
-            const int j0 = kt * MF_BN;
+            const int j0 = kt * BN;
             float s[32];
 #pragma unroll
             for (int e = 0; e < 32; ++e) s[e] = sacc[e >> 4][e & 15];
 
-            const bool full = !DENSE && fa_tile_full(g, i0, i_last, j0, MF_BN);
+            const bool full = !DENSE && fa_tile_full(g, wrow0, wlast, j0, BN);
             if (!full) {
                 if (DENSE) {
 #pragma unroll
@@ -310,7 +357,7 @@ fa_fwd_mfma(const fa_kargs a) {
                 for (int e = 0; e < 32; ++e) mx = fmaxf(mx, s[e]);
                 mx *= sl2;
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = pair_max(mx);
             // Rescale only when the row maximum grows by more than 2^8: p stays <= 256, and the
             // final O / l and LSE do not depend on which maximum was used.
             const bool need = mx > m_run + 8.f;
@@ -337,22 +384,28 @@ fa_fwd_mfma(const fa_kargs a) {
                 pop[t] = u32x4{io::pack(p[base + 0], p[base + 1]), io::pack(p[base + 2], p[base + 3]),
                                io::pack(p[base + 4], p[base + 5]), io::pack(p[base + 6], p[base + 7])};
             }
-            // O^T (d x rows) += V^T P^T.
+            // O^T (d x rows) += V^T P^T; the V^T operand is two transpose reads.
+            const char* vbase = reinterpret_cast<const char*>(lds_v[buf]);
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const u32x4 vop = lds_v[buf][lds_idx8(32 * db + ln, 2 * t + hl)];
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(vbase + v_off[0][db] + t * 16 * KCH * 16));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(vbase + v_off[1][db] + t * 16 * KCH * 16));
+                    const u32x4 vop = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                       __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
                     oacc[db] = io::mma(vop, pop[t], oacc[db]);
                 }
             }
-            if (has_next) sstore(buf ^ 1);
+            __builtin_amdgcn_s_waitcnt(0);   // this thread's prefetch has landed in LDS
             __syncthreads();
         }
     }
 
     // Epilogue: O = O / l, LSE = ln2 (m + log2 l); rows with nothing visible give 0 and -inf.
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = pair_sum(l_run);
     if (row_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         if (hl == 0) {
@@ -369,6 +422,342 @@ fa_fwd_mfma(const fa_kargs a) {
                 const u32x2 w = {io::pack(oacc[db][4 * gi + 0] * inv, oacc[db][4 * gi + 1] * inv),
                                  io::pack(oacc[db][4 * gi + 2] * inv, oacc[db][4 * gi + 3] * inv)};
                 *reinterpret_cast<u32x2*>(op + d) = w;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// MFMA kernel, 64 query rows per wave (the fast path).
+//
+// A 256-thread workgroup owns 256 query rows: each wave holds two groups of 32 rows, so every
+// K or V operand read from LDS feeds two MFMAs (half the LDS traffic per flop of the 32-row
+// layout). One wave per SIMD gets the whole register file (Q operands, two S^T tiles, the O^T
+// accumulators). The kv loop is software-pipelined across tiles: while the softmax of tile t
+// runs on the VALU, the MFMAs of S(t+1) = K(t+1) Q^T are already issued, then O += P(t) V(t).
+// K(t+2) and V(t+1) are fetched from HBM during the iteration and parked in LDS at its end, so
+// one barrier per tile suffices. Global loads are buffer loads whose resource ends at the last
+// key the q tile needs: rows beyond it read as zero without touching memory, so the loads need
+// no branches.
+// ------------------------------------------------------------------------------------------
+
+constexpr int W64_BM = FA_MFMA_BM;   // 256 query rows per workgroup
+constexpr int W64_BN = FA_MFMA_BN;   // keys per kv tile
+constexpr int W64_THREADS = 256;
+
+// LDS chunk index for rows of 4 chunks (64 bytes): four rows share a 256-byte line.
+__device__ __forceinline__ int lds_idx4(int r, int c) {
+    const int line = r >> 2;
+    return line * 16 + 4 * (r & 3) + (c ^ (line & 3));
+}
+
+template <int BN>
+__device__ __forceinline__ int vt_idx(int d, int cc) {
+    if constexpr (BN == 64) return lds_idx8(d, cc);
+    else return lds_idx4(d, cc);
+}
+
+template <int D, bool IS_BF16, bool ALIBI, bool DENSE, int BN>
+__global__ __attribute__((amdgpu_flat_work_group_size(W64_THREADS, W64_THREADS),
+                          amdgpu_waves_per_eu(1, 1))) void
+fa_fwd_mfma64(const fa_kargs a) {
+    static_assert(D == 64 || D == 128, "MFMA path covers D = 64 and 128");
+    static_assert(BN == 32 || BN == 64, "kv tile of 32 or 64 keys");
+    using io = mfma_io<IS_BF16>;
+    constexpr int BM = W64_BM, NT = W64_THREADS;
+    constexpr int JB = BN / 32;                // 32-key blocks of S^T per tile
+    constexpr int NS = 16 * JB;                // S values per lane and row group
+    constexpr int PSTEPS = BN / 16;            // k-steps of O^T += V^T P^T
+    constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+    constexpr int KSTEPS = D / 16;             // k-steps of S^T = K Q^T
+    constexpr int DBLK = D / 32;               // 32-row blocks of O^T
+    constexpr int KLOADS = BN * KCH / NT;      // 16-byte K loads per thread and tile
+    constexpr int VUNITS = (BN / 4) * KCH;     // (4 keys x 8 d) V units per tile
+    static_assert(KLOADS >= 1 && VUNITS <= NT, "tile shape");
+
+    __shared__ u32x4 lds_k[2][BN * KCH];
+    __shared__ u32x4 lds_v[2][D * (BN / 8)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int hl = lane >> 5;
+    const int ln = lane & 31;
+
+    int b, h, qt;
+    fa_geom g;
+    fa_decode_item(a, b, h, qt, g);
+    const int i0 = qt * BM;
+    const int i_last = min(i0 + BM, g.sq) - 1;
+    const fa_kv_range kr = fa_tile_kv_range(g, i0, i_last, BN);
+    const int n_tiles = kr.end - kr.begin;
+    const int kv_lim = min(kr.end * BN, g.skv);   // keys past this are never needed
+
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + h * a.q_hs +
+                         (int64_t(g.q_start) + i0) * a.q_rs;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.kv_bs + h * a.kv_hs +
+                         int64_t(g.kv_start) * a.kv_rs;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.kv_bs + h * a.kv_hs +
+                         int64_t(g.kv_start) * a.kv_rs;
+    const int q_rs = int(a.q_rs), kv_rs = int(a.kv_rs);
+
+    // Rows of this lane: group gi holds row i0 + 64 wave + 32 gi + ln.
+    const int wrow0 = i0 + wave * 64;
+    int row[2], row_lo[2], row_hi[2];
+    bool row_ok[2];
+    u32x4 qop[2][KSTEPS];
+    {
+        const int rows_q = g.sq - i0;   // >= 1
+        const __amdgpu_buffer_rsrc_t rq = fa_rsrc(qp, ((min(rows_q, BM) - 1) * q_rs + D) * 2);
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int lr = wave * 64 + 32 * gi + ln;
+            row[gi] = i0 + lr;
+            row_ok[gi] = row[gi] < g.sq;
+            row_lo[gi] = fa_row_lo(g, row[gi]);
+            row_hi[gi] = fa_row_hi(g, row[gi]);
+#pragma unroll
+            for (int t = 0; t < KSTEPS; ++t) qop[gi][t] = fa_bload(rq, (lr * q_rs + 16 * t + 8 * hl) * 2);
+        }
+    }
+    const float sl2 = a.scale_log2;
+    float slope2 = 0.f;
+    if (ALIBI) slope2 = a.slopes[h] * kLog2e;
+    const int off = g.skv - g.sq;
+    const uint8_t* mrow[2] = {nullptr, nullptr};
+    if (DENSE) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+            mrow[gi] = a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok[gi] ? row[gi] : 0) * a.m_rs;
+    }
+    const int wlast = min(wrow0 + 63, g.sq - 1);   // last valid row of this wave (may be < wrow0)
+
+    float m_run[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+    f32x16 oacc[2][DBLK];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) oacc[gi][db] = f32x16{};
+
+    u32x4 kreg[KLOADS];
+    u32x4 vreg[4];
+
+    auto tile_rsrc = [&](const uint16_t* base, int kt) {
+        const int j0 = kt * BN;
+        const int rows = min(BN, kv_lim - j0);
+        const int bytes = rows > 0 ? ((rows - 1) * kv_rs + D) * 2 : 0;
+        return fa_rsrc(base + int64_t(j0) * kv_rs, bytes);
+    };
+    auto gload_k = [&](int kt) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(kp, kt);
+#pragma unroll
+        for (int p = 0; p < KLOADS; ++p) {
+            const int ci = p * NT + tid;
+            kreg[p] = fa_bload(r, ((ci / KCH) * kv_rs + (ci % KCH) * 8) * 2);
+        }
+    };
+    auto gload_v = [&](int kt) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(vp, kt);
+        if (tid < VUNITS) {
+            const int dc = tid % KCH, jq = tid / KCH;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) vreg[q] = fa_bload(r, ((4 * jq + q) * kv_rs + dc * 8) * 2);
+        }
+    };
+    auto store_k = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < KLOADS; ++p) {
+            const int ci = p * NT + tid;
+            const int r = ci / KCH, c = ci % KCH;
+            lds_k[buf][KCH == 16 ? lds_idx16(r, c) : lds_idx8(r, c)] = kreg[p];
+        }
+    };
+    // V^T[d][key position]; inside each group of 16 keys, bits 2 and 3 of the position are
+    // swapped so that the 8 keys a lane needs for one PV k-step share a 16-byte chunk.
+    auto store_v = [&](int buf) {
+        if (tid < VUNITS) {
+            const int dc = tid % KCH, jq = tid / KCH;
+            const int jm = jq & 3;
+            const int jpos = 16 * (jq >> 2) + 8 * (jm & 1) + 4 * (jm >> 1);
+            const int cc = jpos >> 3, half = (jpos >> 2) & 1;
+            u32x2* vv = reinterpret_cast<u32x2*>(lds_v[buf]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
+                const u32x2 ev = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
+                const u32x2 od = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
+                const int d = 8 * dc + 2 * w;
+                vv[2 * vt_idx<BN>(d, cc) + half] = ev;
+                vv[2 * vt_idx<BN>(d + 1, cc) + half] = od;
+            }
+        }
+    };
+    // S^T for both row groups from K buffer `kb`; each K operand feeds two MFMAs.
+    auto qk = [&](int kb, f32x16 (&s)[2][JB]) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) s[gi][jb] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+                const int r = 32 * jb + ln;
+                const u32x4 kop = lds_k[kb][KCH == 16 ? lds_idx16(r, 2 * t + hl) : lds_idx8(r, 2 * t + hl)];
+                s[0][jb] = io::mma(kop, qop[0][t], s[0][jb]);
+                s[1][jb] = io::mma(kop, qop[1][t], s[1][jb]);
+            }
+        }
+    };
+    auto mask_tile = [&](int j0, f32x16 (&s)[2][JB]) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            if (DENSE) {
+#pragma unroll
+                for (int e = 0; e < NS; ++e) {
+                    const int r = e & 15;
+                    const int j = j0 + 32 * (e >> 4) + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    const bool vis = row_ok[gi] && j < g.skv && mrow[gi][j] == 0;
+                    s[gi][e >> 4][r] = vis ? s[gi][e >> 4][r] : -INFINITY;
+                }
+            } else {
+                const int lo_rel = row_lo[gi] - j0 - 4 * hl;
+                const int hi_rel = row_hi[gi] - j0 - 4 * hl;
+#pragma unroll
+                for (int e = 0; e < NS; ++e) {
+                    const int r = e & 15;
+                    const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
+                    s[gi][e >> 4][r] = (kc >= lo_rel && kc <= hi_rel) ? s[gi][e >> 4][r] : -INFINITY;
+                }
+            }
+        }
+    };
+
+    f32x16 sA[2][JB], sB[2][JB];
+
+    // One kv tile: softmax of s_cur (tile kt), S of tile kt+1 into s_nxt when NEXT, PV of kt.
+    auto step = [&](auto next_tag, int it, f32x16 (&s_cur)[2][JB], f32x16 (&s_nxt)[2][JB]) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        const int kt = kr.begin + it;
+        const int j0 = kt * BN;
+        gload_k(kt + 2);
+        gload_v(kt + 1);
+        const bool partial = DENSE || !fa_tile_full(g, wrow0, wlast, j0, BN);
+        if (partial) mask_tile(j0, s_cur);
+        if constexpr (NEXT) qk((it + 1) & 1, s_nxt);
+
+        u32x4 pop[2][PSTEPS];
+        float alpha[2];
+        bool need[2];
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            float mx = -INFINITY;
+            if (ALIBI) {
+                const float base = slope2 * float(j0 + 4 * hl - row[gi] - off);
+#pragma unroll
+                for (int e = 0; e < NS; ++e) {
+                    const int r = e & 15;
+                    const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
+                    s_cur[gi][e >> 4][r] = fmaf(s_cur[gi][e >> 4][r], sl2, fmaf(slope2, float(kc), base));
+                    mx = fmaxf(mx, s_cur[gi][e >> 4][r]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < NS; ++e) mx = fmaxf(mx, s_cur[gi][e >> 4][e & 15]);
+                mx *= sl2;
+            }
+            mx = pair_max(mx);
+            // Rescale only when the row maximum grows by more than 2^8 (p stays <= 256); O / l
+            // and the LSE do not depend on which maximum was used.
+            need[gi] = mx > m_run[gi] + 8.f;
+            alpha[gi] = need[gi] ? exp2f(m_run[gi] - mx) : 1.f;
+            m_run[gi] = need[gi] ? mx : m_run[gi];
+            const float m_use = m_run[gi] == -INFINITY ? 0.f : m_run[gi];
+            float p[NS];
+            float lsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < NS; ++e) {
+                const float x = s_cur[gi][e >> 4][e & 15];
+                p[e] = ALIBI ? __builtin_amdgcn_exp2f(x - m_use) : __builtin_amdgcn_exp2f(fmaf(x, sl2, -m_use));
+                lsum += p[e];
+            }
+            l_run[gi] = fmaf(l_run[gi], alpha[gi], lsum);
+#pragma unroll
+            for (int t = 0; t < PSTEPS; ++t) {
+                const int base = 16 * (t >> 1) + 8 * (t & 1);
+                pop[gi][t] = u32x4{io::pack(p[base + 0], p[base + 1]), io::pack(p[base + 2], p[base + 3]),
+                                   io::pack(p[base + 4], p[base + 5]), io::pack(p[base + 6], p[base + 7])};
+            }
+        }
+        if (__any(need[0] || need[1])) {
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db) oacc[gi][db] *= alpha[gi];
+        }
+        // O^T += V^T P^T for both groups; each V operand feeds two MFMAs.
+        const int vb = it & 1;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+            for (int t = 0; t < PSTEPS; ++t) {
+                const u32x4 vop = lds_v[vb][vt_idx<BN>(32 * db + ln, 2 * t + hl)];
+                oacc[0][db] = io::mma(vop, pop[0][t], oacc[0][db]);
+                oacc[1][db] = io::mma(vop, pop[1][t], oacc[1][db]);
+            }
+        }
+        store_k(it & 1);
+        store_v((it + 1) & 1);
+        __syncthreads();
+    };
+
+    if (n_tiles > 0) {
+        gload_k(kr.begin);
+        gload_v(kr.begin);
+        store_k(0);
+        store_v(0);
+        gload_k(kr.begin + 1);
+        store_k(1);
+        __syncthreads();
+        qk(0, sA);
+        __syncthreads();   // K buffer 0 is refilled in the first step
+        using yes = std::integral_constant<bool, true>;
+        using no = std::integral_constant<bool, false>;
+        int it = 0;
+        for (; it + 2 < n_tiles; it += 2) {
+            step(yes{}, it, sA, sB);
+            step(yes{}, it + 1, sB, sA);
+        }
+        if (it + 1 < n_tiles) {
+            step(yes{}, it, sA, sB);
+            step(no{}, it + 1, sB, sA);
+        } else {
+            step(no{}, it, sA, sB);
+        }
+    }
+
+    // Epilogue: O = O / l, LSE = ln2 (m + log2 l); rows with nothing visible give 0 and -inf.
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+        const float l_tot = pair_sum(l_run[gi]);
+        if (row_ok[gi]) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            if (hl == 0) {
+                a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + row[gi]] =
+                    l_tot > 0.f ? (m_run[gi] + log2f(l_tot)) * kLn2 : -INFINITY;
+            }
+            uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.q_bs + h * a.q_hs +
+                           (int64_t(g.q_start) + row[gi]) * a.q_rs;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d = 32 * db + 8 * q4 + 4 * hl;
+                    const u32x2 w = {io::pack(oacc[gi][db][4 * q4 + 0] * inv, oacc[gi][db][4 * q4 + 1] * inv),
+                                     io::pack(oacc[gi][db][4 * q4 + 2] * inv, oacc[gi][db][4 * q4 + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(op + d) = w;
+                }
             }
         }
     }
@@ -557,7 +946,7 @@ fa_status upload_tables(const fa_plan& p, void* workspace, hipStream_t stream) {
 }
 
 template <int D, bool BF>
-void launch_mfma_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipStream_t s) {
+void launch_mfma32_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipStream_t s) {
     const dim3 block(MF_THREADS);
     if (alibi) {
         if (dense) fa_fwd_mfma<D, BF, true, true><<<grid, block, 0, s>>>(a);
@@ -565,6 +954,18 @@ void launch_mfma_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipStre
     } else {
         if (dense) fa_fwd_mfma<D, BF, false, true><<<grid, block, 0, s>>>(a);
         else fa_fwd_mfma<D, BF, false, false><<<grid, block, 0, s>>>(a);
+    }
+}
+
+template <int D, bool BF>
+void launch_mfma64_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipStream_t s) {
+    const dim3 block(W64_THREADS);
+    if (alibi) {
+        if (dense) fa_fwd_mfma64<D, BF, true, true, W64_BN><<<grid, block, 0, s>>>(a);
+        else fa_fwd_mfma64<D, BF, true, false, W64_BN><<<grid, block, 0, s>>>(a);
+    } else {
+        if (dense) fa_fwd_mfma64<D, BF, false, true, W64_BN><<<grid, block, 0, s>>>(a);
+        else fa_fwd_mfma64<D, BF, false, false, W64_BN><<<grid, block, 0, s>>>(a);
     }
 }
 
@@ -617,7 +1018,8 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
         std::fprintf(stderr,
                      "[fa] kernel=%s bm=%d bn=%d items/head=%lld blocks=%lld kv tiles visited/full/"
                      "dense=%lld/%lld/%lld table=%d reverse=%d ws=%zu\n",
-                     p.kernel == FA_KERNEL_MFMA ? "mfma" : "generic", p.bm, p.bn,
+                     p.kernel == FA_KERNEL_MFMA ? "mfma64" : (p.kernel == FA_KERNEL_MFMA32 ? "mfma32" : "generic"),
+                     p.bm, p.bn,
                      (long long)p.n_items, (long long)nblocks, (long long)p.kv_tiles_visited,
                      (long long)p.kv_tiles_full, (long long)p.kv_tiles_total, int(p.table),
                      p.reverse_qt, p.ws_bytes);
@@ -632,11 +1034,20 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     if (p.kernel == FA_KERNEL_MFMA) {
         const bool bf = dims->dtype == FA_DTYPE_BF16;
         if (p.D == 128) {
-            if (bf) launch_mfma_d<128, true>(a, alibi, dense, grid, s);
-            else launch_mfma_d<128, false>(a, alibi, dense, grid, s);
+            if (bf) launch_mfma64_d<128, true>(a, alibi, dense, grid, s);
+            else launch_mfma64_d<128, false>(a, alibi, dense, grid, s);
         } else {
-            if (bf) launch_mfma_d<64, true>(a, alibi, dense, grid, s);
-            else launch_mfma_d<64, false>(a, alibi, dense, grid, s);
+            if (bf) launch_mfma64_d<64, true>(a, alibi, dense, grid, s);
+            else launch_mfma64_d<64, false>(a, alibi, dense, grid, s);
+        }
+    } else if (p.kernel == FA_KERNEL_MFMA32) {
+        const bool bf = dims->dtype == FA_DTYPE_BF16;
+        if (p.D == 128) {
+            if (bf) launch_mfma32_d<128, true>(a, alibi, dense, grid, s);
+            else launch_mfma32_d<128, false>(a, alibi, dense, grid, s);
+        } else {
+            if (bf) launch_mfma32_d<64, true>(a, alibi, dense, grid, s);
+            else launch_mfma32_d<64, false>(a, alibi, dense, grid, s);
         }
     } else {
         switch (dims->dtype) {

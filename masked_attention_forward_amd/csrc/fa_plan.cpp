@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 
 namespace {
@@ -25,8 +26,17 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-bool mfma_eligible(int32_t dtype, int64_t D) {
-    return (dtype == FA_DTYPE_F16 || dtype == FA_DTYPE_BF16) && (D == 64 || D == 128);
+// The MFMA kernels address a tile with 32-bit byte offsets: 256 rows of the widest row
+// stride (N * D elements for BSND / TND) must stay below 2^31 bytes.
+bool mfma_eligible(int32_t dtype, int64_t N, int64_t D) {
+    return (dtype == FA_DTYPE_F16 || dtype == FA_DTYPE_BF16) && (D == 64 || D == 128) &&
+           N * D * 2 * 256 < (int64_t(1) << 31);
+}
+
+// FA_KERNEL=mfma64 selects the 64-rows-per-wave MFMA kernel (kept for comparisons).
+bool prefer_mfma64() {
+    const char* e = std::getenv("FA_KERNEL");
+    return e && std::strcmp(e, "mfma64") == 0;
 }
 
 }  // namespace
@@ -140,9 +150,20 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     p.B = int32_t(B);
     p.N = int32_t(d.N);
     p.D = int32_t(d.D);
-    p.kernel = mfma_eligible(d.dtype, d.D) ? FA_KERNEL_MFMA : FA_KERNEL_GENERIC;
-    p.bm = p.kernel == FA_KERNEL_MFMA ? FA_MFMA_BM : FA_GEN_BM;
-    p.bn = p.kernel == FA_KERNEL_MFMA ? FA_MFMA_BN : FA_GEN_BN;
+    p.kernel = FA_KERNEL_GENERIC;
+    p.bm = FA_GEN_BM;
+    p.bn = FA_GEN_BN;
+    if (mfma_eligible(d.dtype, d.N, d.D)) {
+        if (prefer_mfma64()) {
+            p.kernel = FA_KERNEL_MFMA;
+            p.bm = FA_MFMA_BM;
+            p.bn = FA_MFMA_BN;
+        } else {
+            p.kernel = FA_KERNEL_MFMA32;
+            p.bm = FA_MFMA32_BM;
+            p.bn = FA_MFMA32_BN;
+        }
+    }
     for (int64_t b = 0; b < B; ++b) {
         p.rows_total += sq[b];
         p.kv_total += skv[b];
