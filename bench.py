@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--workload", default="causal_8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of attention, time a plain device copy of this many MiB "
+                         "(reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)",
@@ -134,6 +137,15 @@ def main():
     from masked_attention_forward_amd import synth
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": args.warmup + args.steps}))
+        return
     w = synth.workloads()[args.workload]
     q, k, v = (x.to(dev) for x in w.tensors())
     slopes = torch.tensor(w.slopes(), dtype=torch.float32, device=dev) if w.alibi else None

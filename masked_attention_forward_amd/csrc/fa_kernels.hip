@@ -56,6 +56,7 @@ struct fa_kargs {
     int32_t B, N, D;
     int32_t n_qtiles_fixed;
     int32_t reverse_qt;
+    int32_t xcd_major;      // fixed-length launch order, see fa_decode_item
     float scale_log2;       // scale * log2(e)
 };
 
@@ -67,9 +68,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Work item of this workgroup: heads are the fastest index, so the blocks of one (batch, head)
-// always land on the same XCD when N is a multiple of 8 (blocks go round-robin over XCDs);
-// items run heaviest first (the planner sorted the table, or reverse_qt flips the q tiles).
+// Work item of this workgroup. Workgroups are dispatched round-robin over the 8 XCDs, each
+// with its own L2. Table mode (varlen / prefix): heads are the fastest index, so the blocks
+// of one (batch, head) share an XCD when N is a multiple of 8, and items run heaviest first
+// (the planner sorted the table). Fixed-length mode with xcd_major: XCD x = blockIdx % 8
+// works through the (batch, head) pairs congruent to x one pair at a time, heaviest q tile
+// first, so each XCD streams the K/V of about one pair through its L2 at a time.
 // Values read from the workspace tables are the same for every lane; readfirstlane keeps them
 // in scalar registers (buffer descriptors built from them must be wave-uniform).
 __device__ __forceinline__ int fa_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -97,6 +101,13 @@ __device__ __forceinline__ void fa_decode_item(const fa_kargs& a, int& b, int& h
     if (a.items) {
         b = fa_uniform(a.items[2 * item]);
         qt = fa_uniform(a.items[2 * item + 1]);
+    } else if (a.xcd_major) {
+        const int x = w & 7, slot = w >> 3;
+        const int pair = (slot / a.n_qtiles_fixed) * 8 + x;
+        const int r = slot % a.n_qtiles_fixed;
+        b = pair / a.N;
+        h = pair % a.N;
+        qt = a.reverse_qt ? a.n_qtiles_fixed - 1 - r : r;
     } else {
         const int r = item / a.B;
         b = item % a.B;
@@ -169,14 +180,20 @@ __device__ __forceinline__ float pair_sum(float x) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// K and V tiles live in LDS row-major (one row = D keys' worth of 16-byte chunks); chunk c of
-// row j sits at c ^ swz(j). For D = 128 the XOR spreads the 16 rows a 16-lane group reads
-// (ds_read_b128 of K) and the 4 rows x 32 bytes a transpose read of V touches over distinct
-// banks.
+// K and V tiles live in LDS row-major (a row is D/8 chunks of 16 bytes); chunk c of row j
+// sits at c ^ swz(j). D = 128 (256-byte rows): swz swaps the two 2-bit fields of j & 15, a
+// bijection, so the 16 rows one 16-lane group reads with ds_read_b128 (K) land on 16
+// distinct bank groups; and 4 consecutive rows (j & 3 = 0..3) XOR chunk bits 2-3 with
+// distinct values, so the 4 rows x 4 chunks that lanes 0-31 touch with a V transpose read
+// cover all 16 bank groups once. D = 64 (two 128-byte rows per 256-byte line): the same
+// idea on y = j >> 1.
 template <int KCH>
 __device__ __forceinline__ int fa_swz(int j, int c) {
-    if constexpr (KCH == 16) return c ^ (((j & 7) << 1) | ((j >> 3) & 1));
-    else return c ^ ((j >> 1) & 7);
+    if constexpr (KCH == 16) return c ^ (((j & 3) << 2) | ((j >> 2) & 3));
+    else {
+        const int y = j >> 1;
+        return c ^ (((y & 1) << 2) | ((y >> 1) & 3));
+    }
 }
 
 constexpr int MF_BM = FA_MFMA32_BM;   // 128 query rows per workgroup (4 waves x 32 rows)
@@ -204,8 +221,11 @@ fa_fwd_mfma(const fa_kargs a) {
     constexpr int LOADS = TILE_CHUNKS / NT;      // direct loads per thread and tile
     static_assert(LOADS >= 1 && TILE_CHUNKS % NT == 0, "tile shape");
 
-    __shared__ u32x4 lds_k[2][TILE_CHUNKS];
-    __shared__ u32x4 lds_v[2][TILE_CHUNKS];
+    // Two separate buffers per operand (not one array indexed by parity) so the compiler can
+    // see that the prefetch DMA into one buffer never overlaps reads of the other and does not
+    // wait for it before those reads.
+    __shared__ u32x4 lds_k0[TILE_CHUNKS], lds_k1[TILE_CHUNKS];
+    __shared__ u32x4 lds_v0[TILE_CHUNKS], lds_v1[TILE_CHUNKS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -259,6 +279,18 @@ fa_fwd_mfma(const fa_kargs a) {
 
     // HBM -> LDS for one K or V tile: lane l of the wave's p-th load fills physical chunk
     // P = 64 (LOADS wave + p) + l, i.e. row P / KCH, so it fetches that row's logical chunk.
+    // The per-lane source offsets are the same for every tile (only the buffer base moves).
+    // (Kept as scalars: a lambda capturing a local array here made the host compiler drop
+    // this kernel's launch stub.)
+    static_assert(LOADS <= 4, "at most four direct loads per thread and tile");
+    const int wave_u = fa_uniform(wave);
+    auto dl_offset = [&](int p) {
+        const int P = (wave * LOADS + p) * 64 + lane;
+        const int j = P / KCH;
+        return (j * kv_rs + fa_swz<KCH>(j, P % KCH) * 8) * 2;
+    };
+    const int dl0 = dl_offset(0), dl1 = LOADS > 1 ? dl_offset(1) : 0;
+    const int dl2 = LOADS > 2 ? dl_offset(2) : 0, dl3 = LOADS > 3 ? dl_offset(3) : 0;
     auto dload = [&](const uint16_t* base, int kt, u32x4* dst) {
         const int j0 = kt * BN;
         const int rows = min(BN, kv_lim - j0);
@@ -266,12 +298,9 @@ fa_fwd_mfma(const fa_kargs a) {
             fa_rsrc(base + int64_t(j0) * kv_rs, rows > 0 ? ((rows - 1) * kv_rs + D) * 2 : 0);
 #pragma unroll
         for (int p = 0; p < LOADS; ++p) {
-            const int blk = wave * LOADS + p;
-            const int P = blk * 64 + lane;
-            const int j = P / KCH;
-            const int c = fa_swz<KCH>(j, P % KCH);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + blk * 64), 16,
-                                                     (j * kv_rs + c * 8) * 2, 0, 0, 0);
+            const int off = p == 0 ? dl0 : (p == 1 ? dl1 : (p == 2 ? dl2 : dl3));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + (wave_u * LOADS + p) * 64), 16, off,
+                                                     0, 0, 0);
         }
     };
 
@@ -294,33 +323,32 @@ fa_fwd_mfma(const fa_kargs a) {
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) k_off[t] = ln * KCH + fa_swz<KCH>(ln, 2 * t + hl);   // + 32 jb rows
 
-    if (n_tiles > 0) {
-        dload(kp, kr.begin, lds_k[0]);
-        dload(vp, kr.begin, lds_v[0]);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        for (int it = 0; it < n_tiles; ++it) {
-            const int buf = it & 1;
-            const int kt = kr.begin + it;
-            if (it + 1 < n_tiles) {
-                dload(kp, kt + 1, lds_k[buf ^ 1]);
-                dload(vp, kt + 1, lds_v[buf ^ 1]);
+    // S^T of one kv tile from K buffer kb (keys x rows): lane holds row `row`, keys
+    // 32 jb + 8 (r/4) + 4 hl + r%4 of the tile in sacc[jb][r].
+    auto qk = [&](const u32x4* kb, f32x16 (&sacc)[2]) {
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const u32x4 kop = kb[k_off[t] + 32 * jb * KCH];
+                sacc[jb] = io::mma(kop, qop[t], sacc[jb]);
             }
-            // S^T (keys x rows): lane holds row `row`, keys j0 + 32 jb + 8 (r/4) + 4 hl + r%4.
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-            for (int t = 0; t < KSTEPS; ++t) {
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    const u32x4 kop = lds_k[buf][k_off[t] + 32 * jb * KCH];
-                    sacc[jb] = io::mma(kop, qop[t], sacc[jb]);
-                }
-            }
-            const int j0 = kt * BN;
-            float s[32];
-#pragma unroll
-            for (int e = 0; e < 32; ++e) s[e] = sacc[e >> 4][e & 15];
+        }
+    };
 
+    // Tile `it` (its S^T already in s_cur): start the HBM -> LDS loads of K(it+2) and V(it+1),
+    // issue the MFMAs of S^T(it+1) (into s_nxt, when NEXT) so they run while this tile's
+    // softmax is on the VALU, then O += P V(it). K(t) and V(t) live in buffer t % 2.
+    auto step = [&](auto next_tag, int it, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const u32x4* k_next,
+                    const u32x4* v_cur, u32x4* k_fill, u32x4* v_fill) {
+            constexpr bool NEXT = decltype(next_tag)::value;
+            const int kt = kr.begin + it;
+            if (it + 2 < n_tiles) dload(kp, kt + 2, k_fill);
+            if (it + 1 < n_tiles) dload(vp, kt + 1, v_fill);
+            const int j0 = kt * BN;
+            // Per-element masking (partial tiles only) before the next tile's MFMAs are issued.
             const bool full = !DENSE && fa_tile_full(g, wrow0, wlast, j0, BN);
             if (!full) {
                 if (DENSE) {
@@ -329,7 +357,7 @@ fa_fwd_mfma(const fa_kargs a) {
                         const int r = e & 15;
                         const int j = j0 + 32 * (e >> 4) + 8 * (r >> 2) + 4 * hl + (r & 3);
                         const bool vis = row_ok && j < g.skv && mrow[j] == 0;
-                        s[e] = vis ? s[e] : -INFINITY;
+                        s_cur[e >> 4][r] = vis ? s_cur[e >> 4][r] : -INFINITY;
                     }
                 } else {
                     const int lo_rel = row_lo - j0 - 4 * hl;
@@ -338,11 +366,17 @@ fa_fwd_mfma(const fa_kargs a) {
                     for (int e = 0; e < 32; ++e) {
                         const int r = e & 15;
                         const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
-                        s[e] = (kc >= lo_rel && kc <= hi_rel) ? s[e] : -INFINITY;
+                        s_cur[e >> 4][r] = (kc >= lo_rel && kc <= hi_rel) ? s_cur[e >> 4][r] : -INFINITY;
                     }
                 }
             }
-            float mx = -INFINITY;
+            if constexpr (NEXT) qk(k_next, s_nxt);
+            float s[32];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) s[e] = s_cur[e >> 4][e & 15];
+            // Row maximum over this lane's 32 keys in four independent chains (short dependency
+            // chains keep the VALU busy), then across the lane pair.
+            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             if (ALIBI) {
                 const float base = slope2 * float(j0 + 4 * hl - row - off);
 #pragma unroll
@@ -350,32 +384,30 @@ fa_fwd_mfma(const fa_kargs a) {
                     const int r = e & 15;
                     const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
                     s[e] = fmaf(s[e], sl2, fmaf(slope2, float(kc), base));
-                    mx = fmaxf(mx, s[e]);
+                    m4[e & 3] = fmaxf(m4[e & 3], s[e]);
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < 32; ++e) mx = fmaxf(mx, s[e]);
-                mx *= sl2;
+                for (int e = 0; e < 32; ++e) m4[e & 3] = fmaxf(m4[e & 3], s[e]);
             }
+            float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+            if (!ALIBI) mx *= sl2;
             mx = pair_max(mx);
             // Rescale only when the row maximum grows by more than 2^8: p stays <= 256, and the
             // final O / l and LSE do not depend on which maximum was used.
             const bool need = mx > m_run + 8.f;
-            if (__any(need)) {
-                const float alpha = need ? exp2f(m_run - mx) : 1.f;
-                if (need) m_run = mx;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
-            }
+            const float alpha = need ? exp2f(m_run - mx) : 1.f;
+            m_run = need ? mx : m_run;
             const float m_use = m_run == -INFINITY ? 0.f : m_run;
             float p[32];
+            float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 32; ++e) {
                 p[e] = ALIBI ? __builtin_amdgcn_exp2f(s[e] - m_use)
                              : __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -m_use));
-                l_run += p[e];
+                l4[e & 3] += p[e];
             }
+            l_run = fmaf(l_run, alpha, (l4[0] + l4[1]) + (l4[2] + l4[3]));
             // P^T as the B operand: k-step t takes accumulator entries 8 (t%2) .. +7 of block t/2.
             u32x4 pop[4];
 #pragma unroll
@@ -384,12 +416,33 @@ fa_fwd_mfma(const fa_kargs a) {
                 pop[t] = u32x4{io::pack(p[base + 0], p[base + 1]), io::pack(p[base + 2], p[base + 3]),
                                io::pack(p[base + 4], p[base + 5]), io::pack(p[base + 6], p[base + 7])};
             }
-            // O^T (d x rows) += V^T P^T; the V^T operand is two transpose reads.
-            const char* vbase = reinterpret_cast<const char*>(lds_v[buf]);
+            // Keep the softmax above the rescale branch below (otherwise it sinks towards its
+            // only use, the PV MFMAs, and lands outside the block it is interleaved with).
 #pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
+            for (int t = 0; t < 4; ++t) asm volatile("" : : "v"(pop[t]));
+            asm volatile("" : : "v"(l_run));
+            // Interleave: the MFMAs of the next tile's S^T (when NEXT) with this tile's softmax
+            // VALU work, K operand reads running four ahead.
+            if constexpr (NEXT) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
+                for (int i = 0; i < 2 * KSTEPS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                    if (i + 4 < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            if (__any(need)) {
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+            }
+            // O^T (d x rows) += V^T P^T; the V^T operand is two transpose reads. Consecutive
+            // MFMAs go to different accumulators (t outer, db inner) so none waits on the last.
+            const char* vbase = reinterpret_cast<const char*>(v_cur);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db) {
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) s16x4*)(vbase + v_off[0][db] + t * 16 * KCH * 16));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -399,8 +452,38 @@ fa_fwd_mfma(const fa_kargs a) {
                     oacc[db] = io::mma(vop, pop[t], oacc[db]);
                 }
             }
-            __builtin_amdgcn_s_waitcnt(0);   // this thread's prefetch has landed in LDS
+            // PV: keep the transpose reads two MFMAs ahead.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+            for (int i = 0; i < 4 * DBLK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                if (i + 2 < 4 * DBLK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // this thread's loads have landed in LDS
             __syncthreads();
+    };
+
+    if (n_tiles > 0) {
+        using yes = std::integral_constant<bool, true>;
+        using no = std::integral_constant<bool, false>;
+        dload(kp, kr.begin, lds_k0);
+        dload(vp, kr.begin, lds_v0);
+        if (n_tiles > 1) dload(kp, kr.begin + 1, lds_k1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        f32x16 sA[2], sB[2];
+        qk(lds_k0, sA);
+        __syncthreads();   // K buffer 0 is refilled with K(2) during tile 0
+        int it = 0;
+        for (; it + 2 < n_tiles; it += 2) {
+            step(yes{}, it, sA, sB, lds_k1, lds_v0, lds_k0, lds_v1);
+            step(yes{}, it + 1, sB, sA, lds_k0, lds_v1, lds_k1, lds_v0);
+        }
+        if (it + 1 < n_tiles) {
+            step(yes{}, it, sA, sB, lds_k1, lds_v0, lds_k0, lds_v1);
+            step(no{}, it + 1, sB, sA, lds_k0, lds_v1, lds_k1, lds_v0);
+        } else {
+            step(no{}, it, sA, sB, lds_k1, lds_v0, lds_k0, lds_v1);
         }
     }
 
@@ -926,6 +1009,7 @@ fa_kargs make_kargs(const fa_plan& p, const void* q, const void* k, const void* 
     a.D = p.D;
     a.n_qtiles_fixed = p.n_qtiles_fixed;
     a.reverse_qt = p.reverse_qt;
+    a.xcd_major = p.xcd_major;
     a.scale_log2 = scale * kLog2e;
     return a;
 }
@@ -1017,12 +1101,12 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     if (log_enabled()) {
         std::fprintf(stderr,
                      "[fa] kernel=%s bm=%d bn=%d items/head=%lld blocks=%lld kv tiles visited/full/"
-                     "dense=%lld/%lld/%lld table=%d reverse=%d ws=%zu\n",
+                     "dense=%lld/%lld/%lld table=%d reverse=%d xcd_major=%d ws=%zu\n",
                      p.kernel == FA_KERNEL_MFMA ? "mfma64" : (p.kernel == FA_KERNEL_MFMA32 ? "mfma32" : "generic"),
                      p.bm, p.bn,
                      (long long)p.n_items, (long long)nblocks, (long long)p.kv_tiles_visited,
                      (long long)p.kv_tiles_full, (long long)p.kv_tiles_total, int(p.table),
-                     p.reverse_qt, p.ws_bytes);
+                     p.reverse_qt, p.xcd_major, p.ws_bytes);
     }
     st = upload_tables(p, workspace, s);
     if (st != FA_OK) return st;

@@ -283,6 +283,8 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         p.ws_bytes = 0;
         if (B > 0 && p.n_qtiles_fixed > 1 && !sizes_only)
             p.reverse_qt = item_cost(0, p.n_qtiles_fixed - 1, nullptr) > item_cost(0, 0, nullptr);
+        const char* xm = std::getenv("FA_XCD_MAJOR");
+        p.xcd_major = ((B * d.N) % 8 == 0 && !(xm && xm[0] == '0')) ? 1 : 0;
     }
 
     if (with_tables && !sizes_only) {
