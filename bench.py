@@ -27,23 +27,32 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+# Sources that decide the dominant kernel's memory traffic (its code and its launch order).
 KERNEL_SOURCES = ["masked_attention_forward_amd/csrc/fa_kernels.hip",
-                  "masked_attention_forward_amd/csrc/fa_mask.h"]
+                  "masked_attention_forward_amd/csrc/fa_mask.h",
+                  "masked_attention_forward_amd/csrc/fa_plan.cpp",
+                  "masked_attention_forward_amd/csrc/fa_plan.h"]
+DOMINANT_KERNEL = "fa_fwd_pp"
 METRIC = "effective TFLOP/s (unmasked FLOPs) attn fwd bf16 D=128; % of MFMA peak"
 
 
 def kernel_sources_sha() -> str:
+    """Hash of the code lines of KERNEL_SOURCES (full-line comments and blank lines skipped, so
+    a comment edit does not invalidate recorded counters; any code change does)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+            for line in f:
+                t = line.strip()
+                if t and not t.startswith(b"//"):
+                    h.update(t + b"\n")
     return h.hexdigest()[:16]
 
 
 def recorded_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"fa_fwd_mfma_{workload}_counters.md")
+    path = os.path.join(ROOT, "profiles", f"{DOMINANT_KERNEL}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -122,7 +131,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="causal_8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=48,
+                    help="(batch, head) slices of the workload the CPU oracle is timed on")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(reference for the HBM byte counters)")

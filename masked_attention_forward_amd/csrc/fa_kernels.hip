@@ -8,20 +8,23 @@
 // column intervals by fa_mask.h; the alibi bias is "压缩mask"'s per-head slope times a
 // right-aligned relative position.
 //
-// Two kernel families:
-//  * fa_fwd_mfma: fp16 / bf16, D in {64, 128}. A 256-thread workgroup owns 128 query rows
-//    (4 waves x 32 rows). Each kv tile is 64 keys. Per wave and tile it computes
-//    S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}, so each lane ends up holding one query
-//    row (and 32 of the tile's 64 keys); softmax statistics are lane-local plus one exchange
-//    with lane^32. Then O^T += V^T P^T with the same MFMA, P taken straight from the S^T
-//    accumulators (no data movement), V^T read from an LDS copy that was transposed on the
-//    way in. K and V tiles are double-buffered in LDS with 128-bit coalesced global loads
-//    prefetched one tile ahead; LDS layouts are XOR-swizzled so the 16-byte operand reads
-//    hit distinct banks.
+// Kernels:
+//  * fa_fwd_pp (default for fp16 / bf16, D in {64, 128}): 512-thread workgroups own 256 query
+//    rows (8 waves x 32 rows). Two groups of four waves alternate phases at workgroup barriers:
+//    while one group runs its MFMAs (O^T += V^T P^T, then S^T = K Q^T for the next tile) the
+//    other runs the softmax on the VALU, and waves w and w + 4 share a SIMD, so every SIMD
+//    overlaps one wave's matrix work with the other's exponentials.
+//  * fa_fwd_mfma (same inputs; selected with FA_KERNEL=mfma32): 256-thread workgroups of 128
+//    rows, two per CU, software-pipelined within each wave instead of across waves.
+//    Both MFMA kernels compute S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}, so each lane
+//    holds one query row (and 32 of the tile's 64 keys): softmax statistics are lane-local plus
+//    one exchange with lane^32, and P^T is taken straight from the S^T accumulators. K and V
+//    tiles go from HBM straight into XOR-swizzled LDS with buffer loads; the V^T operand is
+//    read with ds_read_b64_tr_b16 transpose reads.
 //  * fa_fwd_generic: any dtype (fp32 included), D <= 128. One thread per query row, fp32
 //    throughout (P is never rounded), K/V tiles of 16 keys staged in LDS.
-// Both visit only kv tiles that hold a visible entry (fa_tile_kv_range) and skip
-// per-element masking on tiles that are fully visible (fa_tile_full).
+// All visit only kv tiles that hold a visible entry (fa_tile_kv_range) and skip per-element
+// masking on tiles that are fully visible (fa_tile_full).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -511,61 +514,64 @@ fa_fwd_mfma(const fa_kargs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// MFMA kernel, 64 query rows per wave (the fast path).
+// MFMA ping-pong kernel (the fast path).
 //
-// A 256-thread workgroup owns 256 query rows: each wave holds two groups of 32 rows, so every
-// K or V operand read from LDS feeds two MFMAs (half the LDS traffic per flop of the 32-row
-// layout). One wave per SIMD gets the whole register file (Q operands, two S^T tiles, the O^T
-// accumulators). The kv loop is software-pipelined across tiles: while the softmax of tile t
-// runs on the VALU, the MFMAs of S(t+1) = K(t+1) Q^T are already issued, then O += P(t) V(t).
-// K(t+2) and V(t+1) are fetched from HBM during the iteration and parked in LDS at its end, so
-// one barrier per tile suffices. Global loads are buffer loads whose resource ends at the last
-// key the q tile needs: rows beyond it read as zero without touching memory, so the loads need
-// no branches.
+// A 512-thread workgroup owns 256 query rows, 32 per wave; waves w and w + 4 share a SIMD.
+// Group A (waves 0-3) and group B (waves 4-7) run the same sequence of phases,
+//     QK(0) | SM(0) | MM(0) | SM(1) | MM(1) | ... | SM(n-1) | MM(n-1)
+// with B one phase behind A and a workgroup barrier between phases. SM(t) is the masked
+// online softmax of kv tile t (VALU only); MM(t) is O^T += V(t)^T P(t)^T followed by
+// S^T(t+1) = K(t+1) Q^T (matrix core only). In every phase one group runs MFMAs while its
+// partner on the same SIMD runs the softmax, so the exponentials hide under the matrix work
+// instead of alternating with it.
+//
+// Tile data: set u = {K(u), V(u-1)} is what MM(u-1) reads, in phase 2u of A and 2u + 1 of B.
+// Two LDS buffers hold sets u and u + 1; set u + 2 goes HBM -> LDS (direct buffer loads)
+// into the buffer of set u as soon as both groups are done with it, two phases before it is
+// needed. Each group issues its half of the loads at the start of the phase in which set
+// u + 2 becomes writable and waits for them (vmcnt) at the end of the following phase.
+// Phase barriers order LDS only, so loads stay in flight across them.
 // ------------------------------------------------------------------------------------------
 
-constexpr int W64_BM = FA_MFMA_BM;   // 256 query rows per workgroup
-constexpr int W64_BN = FA_MFMA_BN;   // keys per kv tile
-constexpr int W64_THREADS = 256;
+constexpr int PP_BM = FA_PP_BM;   // 256 query rows per workgroup (8 waves x 32 rows)
+constexpr int PP_BN = FA_PP_BN;   // 64 keys per kv tile
+constexpr int PP_THREADS = 512;
 
-// LDS chunk index for rows of 4 chunks (64 bytes): four rows share a 256-byte line.
-__device__ __forceinline__ int lds_idx4(int r, int c) {
-    const int line = r >> 2;
-    return line * 16 + 4 * (r & 3) + (c ^ (line & 3));
+// Phase barrier: waits for this wave's LDS reads (lgkmcnt 0) but not for its direct-to-LDS
+// loads (vmcnt), which are waited for explicitly in the phase before their data is read; a
+// memory fence here would wait for those loads too. The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void fa_lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left alone
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-template <int BN>
-__device__ __forceinline__ int vt_idx(int d, int cc) {
-    if constexpr (BN == 64) return lds_idx8(d, cc);
-    else return lds_idx4(d, cc);
-}
-
-template <int D, bool IS_BF16, bool ALIBI, bool DENSE, int BN>
-__global__ __attribute__((amdgpu_flat_work_group_size(W64_THREADS, W64_THREADS),
-                          amdgpu_waves_per_eu(1, 1))) void
-fa_fwd_mfma64(const fa_kargs a) {
+template <int D, bool IS_BF16, bool ALIBI, bool DENSE>
+__global__ __attribute__((amdgpu_flat_work_group_size(PP_THREADS, PP_THREADS),
+                          amdgpu_waves_per_eu(2, 2))) void
+fa_fwd_pp(const fa_kargs a) {
     static_assert(D == 64 || D == 128, "MFMA path covers D = 64 and 128");
-    static_assert(BN == 32 || BN == 64, "kv tile of 32 or 64 keys");
     using io = mfma_io<IS_BF16>;
-    constexpr int BM = W64_BM, NT = W64_THREADS;
-    constexpr int JB = BN / 32;                // 32-key blocks of S^T per tile
-    constexpr int NS = 16 * JB;                // S values per lane and row group
-    constexpr int PSTEPS = BN / 16;            // k-steps of O^T += V^T P^T
-    constexpr int KCH = D / 8;                 // 16-byte chunks per K row
-    constexpr int KSTEPS = D / 16;             // k-steps of S^T = K Q^T
-    constexpr int DBLK = D / 32;               // 32-row blocks of O^T
-    constexpr int KLOADS = BN * KCH / NT;      // 16-byte K loads per thread and tile
-    constexpr int VUNITS = (BN / 4) * KCH;     // (4 keys x 8 d) V units per tile
-    static_assert(KLOADS >= 1 && VUNITS <= NT, "tile shape");
+    constexpr int BM = PP_BM, BN = PP_BN, NT = PP_THREADS;
+    constexpr int KCH = D / 8;                   // 16-byte chunks per K / V row
+    constexpr int KSTEPS = D / 16;               // k-steps of S^T = K Q^T
+    constexpr int DBLK = D / 32;                 // 32-row blocks of O^T
+    constexpr int TILE_CHUNKS = BN * KCH;        // 16-byte chunks per K or V tile
+    constexpr int LOADS = TILE_CHUNKS / NT;      // direct loads per thread and tile
+    static_assert(LOADS >= 1 && LOADS <= 2 && TILE_CHUNKS % NT == 0, "tile shape");
 
-    __shared__ u32x4 lds_k[2][BN * KCH];
-    __shared__ u32x4 lds_v[2][D * (BN / 8)];
+    __shared__ u32x4 lds_k0[TILE_CHUNKS], lds_k1[TILE_CHUNKS];
+    __shared__ u32x4 lds_v0[TILE_CHUNKS], lds_v1[TILE_CHUNKS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int hl = lane >> 5;
     const int ln = lane & 31;
+    const int wave_u = fa_uniform(wave);
+    const int grp = wave_u >> 2;   // 0: group A, 1: group B (one phase behind)
 
     int b, h, qt;
     fa_geom g;
@@ -574,7 +580,7 @@ fa_fwd_mfma64(const fa_kargs a) {
     const int i_last = min(i0 + BM, g.sq) - 1;
     const fa_kv_range kr = fa_tile_kv_range(g, i0, i_last, BN);
     const int n_tiles = kr.end - kr.begin;
-    const int kv_lim = min(kr.end * BN, g.skv);   // keys past this are never needed
+    const int kv_lim = min(kr.end * BN, g.skv);
 
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + h * a.q_hs +
                          (int64_t(g.q_start) + i0) * a.q_rs;
@@ -584,266 +590,268 @@ fa_fwd_mfma64(const fa_kargs a) {
                          int64_t(g.kv_start) * a.kv_rs;
     const int q_rs = int(a.q_rs), kv_rs = int(a.kv_rs);
 
-    // Rows of this lane: group gi holds row i0 + 64 wave + 32 gi + ln.
-    const int wrow0 = i0 + wave * 64;
-    int row[2], row_lo[2], row_hi[2];
-    bool row_ok[2];
-    u32x4 qop[2][KSTEPS];
+    const int lrow = wave * 32 + ln;
+    const int row = i0 + lrow;
+    const bool row_ok = row < g.sq;
+    u32x4 qop[KSTEPS];
     {
-        const int rows_q = g.sq - i0;   // >= 1
-        const __amdgpu_buffer_rsrc_t rq = fa_rsrc(qp, ((min(rows_q, BM) - 1) * q_rs + D) * 2);
+        const __amdgpu_buffer_rsrc_t rq = fa_rsrc(qp, ((min(g.sq - i0, BM) - 1) * q_rs + D) * 2);
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            const int lr = wave * 64 + 32 * gi + ln;
-            row[gi] = i0 + lr;
-            row_ok[gi] = row[gi] < g.sq;
-            row_lo[gi] = fa_row_lo(g, row[gi]);
-            row_hi[gi] = fa_row_hi(g, row[gi]);
-#pragma unroll
-            for (int t = 0; t < KSTEPS; ++t) qop[gi][t] = fa_bload(rq, (lr * q_rs + 16 * t + 8 * hl) * 2);
-        }
+        for (int t = 0; t < KSTEPS; ++t) qop[t] = fa_bload(rq, (lrow * q_rs + 16 * t + 8 * hl) * 2);
     }
+    const int row_lo = fa_row_lo(g, row);
+    const int row_hi = fa_row_hi(g, row);
+    const int wrow0 = i0 + wave * 32;
+    const int wlast = min(wrow0 + 31, g.sq - 1);
     const float sl2 = a.scale_log2;
     float slope2 = 0.f;
     if (ALIBI) slope2 = a.slopes[h] * kLog2e;
+    // Load these now: a scalar load left to the loop would be waited for there with
+    // lgkmcnt(0), which also waits for every LDS read in flight.
+    asm volatile("" : : "s"(sl2), "v"(slope2));
     const int off = g.skv - g.sq;
-    const uint8_t* mrow[2] = {nullptr, nullptr};
-    if (DENSE) {
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-            mrow[gi] = a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok[gi] ? row[gi] : 0) * a.m_rs;
-    }
-    const int wlast = min(wrow0 + 63, g.sq - 1);   // last valid row of this wave (may be < wrow0)
+    const uint8_t* mrow = nullptr;
+    if (DENSE) mrow = a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs;
 
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
-    f32x16 oacc[2][DBLK];
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x16 oacc[DBLK];
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) oacc[gi][db] = f32x16{};
+    for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
 
-    u32x4 kreg[KLOADS];
-    u32x4 vreg[4];
-
-    auto tile_rsrc = [&](const uint16_t* base, int kt) {
+    // HBM -> LDS for this thread's share of one K or V tile (physical chunk
+    // 64 (LOADS wave + p) + lane, i.e. row P / KCH, logical chunk un-swizzled).
+    auto dl_offset = [&](int p) __attribute__((always_inline)) {
+        const int P = (wave * LOADS + p) * 64 + lane;
+        const int j = P / KCH;
+        return (j * kv_rs + fa_swz<KCH>(j, P % KCH) * 8) * 2;
+    };
+    const int dl0 = dl_offset(0), dl1 = LOADS > 1 ? dl_offset(1) : 0;
+    auto dload = [&](const uint16_t* base, int kt, u32x4* dst) __attribute__((always_inline)) {
         const int j0 = kt * BN;
         const int rows = min(BN, kv_lim - j0);
-        const int bytes = rows > 0 ? ((rows - 1) * kv_rs + D) * 2 : 0;
-        return fa_rsrc(base + int64_t(j0) * kv_rs, bytes);
-    };
-    auto gload_k = [&](int kt) {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(kp, kt);
+        const __amdgpu_buffer_rsrc_t r =
+            fa_rsrc(base + int64_t(j0) * kv_rs, rows > 0 ? ((rows - 1) * kv_rs + D) * 2 : 0);
 #pragma unroll
-        for (int p = 0; p < KLOADS; ++p) {
-            const int ci = p * NT + tid;
-            kreg[p] = fa_bload(r, ((ci / KCH) * kv_rs + (ci % KCH) * 8) * 2);
+        for (int p = 0; p < LOADS; ++p)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + (wave_u * LOADS + p) * 64), 16,
+                                                     p == 0 ? dl0 : dl1, 0, 0, 0);
+    };
+
+    const int src = lane & 15;
+    const int dlo = 16 * ((lane >> 4) & 1) + 4 * (src & 3);
+    int v_off[2][DBLK];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int j = 8 * h2 + 4 * hl + (src >> 2);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            const int d0 = 32 * db + dlo;
+            v_off[h2][db] = (j * KCH + fa_swz<KCH>(j, d0 >> 3)) * 16 + (d0 & 7) * 2;
         }
-    };
-    auto gload_v = [&](int kt) {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(vp, kt);
-        if (tid < VUNITS) {
-            const int dc = tid % KCH, jq = tid / KCH;
+    }
+    int k_off[KSTEPS];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) vreg[q] = fa_bload(r, ((4 * jq + q) * kv_rs + dc * 8) * 2);
-        }
-    };
-    auto store_k = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < KLOADS; ++p) {
-            const int ci = p * NT + tid;
-            const int r = ci / KCH, c = ci % KCH;
-            lds_k[buf][KCH == 16 ? lds_idx16(r, c) : lds_idx8(r, c)] = kreg[p];
-        }
-    };
-    // V^T[d][key position]; inside each group of 16 keys, bits 2 and 3 of the position are
-    // swapped so that the 8 keys a lane needs for one PV k-step share a 16-byte chunk.
-    auto store_v = [&](int buf) {
-        if (tid < VUNITS) {
-            const int dc = tid % KCH, jq = tid / KCH;
-            const int jm = jq & 3;
-            const int jpos = 16 * (jq >> 2) + 8 * (jm & 1) + 4 * (jm >> 1);
-            const int cc = jpos >> 3, half = (jpos >> 2) & 1;
-            u32x2* vv = reinterpret_cast<u32x2*>(lds_v[buf]);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
-                const u32x2 ev = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-                const u32x2 od = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-                const int d = 8 * dc + 2 * w;
-                vv[2 * vt_idx<BN>(d, cc) + half] = ev;
-                vv[2 * vt_idx<BN>(d + 1, cc) + half] = od;
-            }
-        }
-    };
-    // S^T for both row groups from K buffer `kb`; each K operand feeds two MFMAs.
-    auto qk = [&](int kb, f32x16 (&s)[2][JB]) {
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb) s[gi][jb] = f32x16{};
+    for (int t = 0; t < KSTEPS; ++t) k_off[t] = ln * KCH + fa_swz<KCH>(ln, 2 * t + hl);
+
+    f32x16 sacc[2];   // S^T of the tile waiting for its softmax
+    u32x4 pop[4];     // P^T of the tile waiting for its PV product
+
+    auto qk = [&](const u32x4* kb) __attribute__((always_inline)) {
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) {
 #pragma unroll
-            for (int jb = 0; jb < JB; ++jb) {
-                const int r = 32 * jb + ln;
-                const u32x4 kop = lds_k[kb][KCH == 16 ? lds_idx16(r, 2 * t + hl) : lds_idx8(r, 2 * t + hl)];
-                s[0][jb] = io::mma(kop, qop[0][t], s[0][jb]);
-                s[1][jb] = io::mma(kop, qop[1][t], s[1][jb]);
+            for (int jb = 0; jb < 2; ++jb) {
+                const u32x4 kop = kb[k_off[t] + 32 * jb * KCH];
+                sacc[jb] = io::mma(kop, qop[t], sacc[jb]);
             }
         }
     };
-    auto mask_tile = [&](int j0, f32x16 (&s)[2][JB]) {
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
+
+    // SM(t): mask, scale (+ alibi), online softmax update, P^T packed for the PV product. The
+    // O^T rescale happens here too: no MFMA of this wave is using the accumulators.
+    auto softmax = [&](int t) __attribute__((always_inline)) {
+        const int j0 = (kr.begin + t) * BN;
+        const bool full = !DENSE && fa_tile_full(g, wrow0, wlast, j0, BN);
+        if (!full) {
             if (DENSE) {
+                // One byte per key; keys past Skv (and invalid rows) read nothing.
+                uint32_t hidden = 0;
 #pragma unroll
-                for (int e = 0; e < NS; ++e) {
+                for (int e = 0; e < 32; ++e) {
                     const int r = e & 15;
                     const int j = j0 + 32 * (e >> 4) + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    const bool vis = row_ok[gi] && j < g.skv && mrow[gi][j] == 0;
-                    s[gi][e >> 4][r] = vis ? s[gi][e >> 4][r] : -INFINITY;
+                    const bool in = row_ok && j < g.skv;
+                    hidden |= uint32_t(!in || mrow[in ? j : 0] != 0) << e;
                 }
-            } else {
-                const int lo_rel = row_lo[gi] - j0 - 4 * hl;
-                const int hi_rel = row_hi[gi] - j0 - 4 * hl;
 #pragma unroll
-                for (int e = 0; e < NS; ++e) {
+                for (int e = 0; e < 32; ++e)
+                    sacc[e >> 4][e & 15] = (hidden >> e) & 1u ? -INFINITY : sacc[e >> 4][e & 15];
+            } else {
+                const int lo_rel = row_lo - j0 - 4 * hl;
+                const int hi_rel = row_hi - j0 - 4 * hl;
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
                     const int r = e & 15;
                     const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
-                    s[gi][e >> 4][r] = (kc >= lo_rel && kc <= hi_rel) ? s[gi][e >> 4][r] : -INFINITY;
+                    sacc[e >> 4][r] = (kc >= lo_rel && kc <= hi_rel) ? sacc[e >> 4][r] : -INFINITY;
                 }
             }
+        }
+        float s[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) s[e] = sacc[e >> 4][e & 15];
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (ALIBI) {
+            const float base = slope2 * float(j0 + 4 * hl - row - off);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                const int r = e & 15;
+                const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
+                s[e] = fmaf(s[e], sl2, fmaf(slope2, float(kc), base));
+                m4[e & 3] = fmaxf(m4[e & 3], s[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) m4[e & 3] = fmaxf(m4[e & 3], s[e]);
+        }
+        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        if (!ALIBI) mx *= sl2;
+        mx = pair_max(mx);
+        // Rescale only when the row maximum grows by more than 2^8: p stays <= 256, and the
+        // final O / l and LSE do not depend on which maximum was used.
+        const bool need = mx > m_run + 8.f;
+        const float alpha = need ? exp2f(m_run - mx) : 1.f;
+        m_run = need ? mx : m_run;
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float p[32];
+        float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            p[e] = ALIBI ? __builtin_amdgcn_exp2f(s[e] - m_use) : __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -m_use));
+            l4[e & 3] += p[e];
+        }
+        l_run = fmaf(l_run, alpha, (l4[0] + l4[1]) + (l4[2] + l4[3]));
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int base = 16 * (t4 >> 1) + 8 * (t4 & 1);
+            pop[t4] = u32x4{io::pack(p[base + 0], p[base + 1]), io::pack(p[base + 2], p[base + 3]),
+                            io::pack(p[base + 4], p[base + 5]), io::pack(p[base + 6], p[base + 7])};
+        }
+        if (__any(need)) {
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+        }
+        // The softmax belongs to this phase: keep it from sinking past the barrier.
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) asm volatile("" : : "v"(pop[t4]));
+        asm volatile("" : : "v"(l_run));
+    };
+
+    // MM(t): O^T += V^T P^T from set buffer (vb), then S^T of the next tile from (kb). After
+    // the last tile the S^T product reads a stale K buffer and its result is never used.
+    auto matmul = [&](const u32x4* kb, const u32x4* vb) __attribute__((always_inline)) {
+        const char* vbase = reinterpret_cast<const char*>(vb);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vbase + v_off[0][db] + t * 16 * KCH * 16));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vbase + v_off[1][db] + t * 16 * KCH * 16));
+                const u32x4 vop = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                   __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+                oacc[db] = io::mma(vop, pop[t], oacc[db]);
+            }
+        }
+        qk(kb);
+        // LDS reads run about three MFMAs ahead: six reads up front, then two per PV MFMA
+        // (its two V^T halves) and one per S^T MFMA.
+        constexpr int NPV = 4 * DBLK, NQK = 2 * KSTEPS;
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < NPV + NQK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     };
 
-    f32x16 sA[2][JB], sB[2][JB];
+    // Loads of set t + 2 = {K(t+2), V(t+1)} (the parts that exist) into the free buffer.
+    auto issue = [&](int t, u32x4* kfill, u32x4* vfill) __attribute__((always_inline)) {
+        if (t + 1 < n_tiles) dload(vp, kr.begin + t + 1, vfill);
+        if (t + 2 < n_tiles) dload(kp, kr.begin + t + 2, kfill);
+    };
 
-    // One kv tile: softmax of s_cur (tile kt), S of tile kt+1 into s_nxt when NEXT, PV of kt.
-    auto step = [&](auto next_tag, int it, f32x16 (&s_cur)[2][JB], f32x16 (&s_nxt)[2][JB]) {
-        constexpr bool NEXT = decltype(next_tag)::value;
-        const int kt = kr.begin + it;
-        const int j0 = kt * BN;
-        gload_k(kt + 2);
-        gload_v(kt + 1);
-        const bool partial = DENSE || !fa_tile_full(g, wrow0, wlast, j0, BN);
-        if (partial) mask_tile(j0, s_cur);
-        if constexpr (NEXT) qk((it + 1) & 1, s_nxt);
-
-        u32x4 pop[2][PSTEPS];
-        float alpha[2];
-        bool need[2];
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-            float mx = -INFINITY;
-            if (ALIBI) {
-                const float base = slope2 * float(j0 + 4 * hl - row[gi] - off);
-#pragma unroll
-                for (int e = 0; e < NS; ++e) {
-                    const int r = e & 15;
-                    const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
-                    s_cur[gi][e >> 4][r] = fmaf(s_cur[gi][e >> 4][r], sl2, fmaf(slope2, float(kc), base));
-                    mx = fmaxf(mx, s_cur[gi][e >> 4][r]);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < NS; ++e) mx = fmaxf(mx, s_cur[gi][e >> 4][e & 15]);
-                mx *= sl2;
-            }
-            mx = pair_max(mx);
-            // Rescale only when the row maximum grows by more than 2^8 (p stays <= 256); O / l
-            // and the LSE do not depend on which maximum was used.
-            need[gi] = mx > m_run[gi] + 8.f;
-            alpha[gi] = need[gi] ? exp2f(m_run[gi] - mx) : 1.f;
-            m_run[gi] = need[gi] ? mx : m_run[gi];
-            const float m_use = m_run[gi] == -INFINITY ? 0.f : m_run[gi];
-            float p[NS];
-            float lsum = 0.f;
-#pragma unroll
-            for (int e = 0; e < NS; ++e) {
-                const float x = s_cur[gi][e >> 4][e & 15];
-                p[e] = ALIBI ? __builtin_amdgcn_exp2f(x - m_use) : __builtin_amdgcn_exp2f(fmaf(x, sl2, -m_use));
-                lsum += p[e];
-            }
-            l_run[gi] = fmaf(l_run[gi], alpha[gi], lsum);
-#pragma unroll
-            for (int t = 0; t < PSTEPS; ++t) {
-                const int base = 16 * (t >> 1) + 8 * (t & 1);
-                pop[gi][t] = u32x4{io::pack(p[base + 0], p[base + 1]), io::pack(p[base + 2], p[base + 3]),
-                                   io::pack(p[base + 4], p[base + 5]), io::pack(p[base + 6], p[base + 7])};
-            }
-        }
-        if (__any(need[0] || need[1])) {
-#pragma unroll
-            for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db) oacc[gi][db] *= alpha[gi];
-        }
-        // O^T += V^T P^T for both groups; each V operand feeds two MFMAs.
-        const int vb = it & 1;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-#pragma unroll
-            for (int t = 0; t < PSTEPS; ++t) {
-                const u32x4 vop = lds_v[vb][vt_idx<BN>(32 * db + ln, 2 * t + hl)];
-                oacc[0][db] = io::mma(vop, pop[0][t], oacc[0][db]);
-                oacc[1][db] = io::mma(vop, pop[1][t], oacc[1][db]);
-            }
-        }
-        store_k(it & 1);
-        store_v((it + 1) & 1);
-        __syncthreads();
+    // Iteration t: SM(t) then MM(t); set t + 1 sits in buffer PB.
+    auto iter = [&](auto pb_tag, int t) __attribute__((always_inline)) {
+        constexpr int PB = decltype(pb_tag)::value;
+        const u32x4* kcur = PB ? lds_k1 : lds_k0;
+        const u32x4* vcur = PB ? lds_v1 : lds_v0;
+        u32x4* kfill = PB ? lds_k0 : lds_k1;
+        u32x4* vfill = PB ? lds_v0 : lds_v1;
+        if (grp == 1) issue(t, kfill, vfill);
+        softmax(t);
+        if (grp == 0) __builtin_amdgcn_s_waitcnt(0);   // set t + 1 (issued by A in MM(t-1))
+        fa_lds_barrier();
+        if (grp == 0) issue(t, kfill, vfill);
+        __builtin_amdgcn_s_setprio(1);
+        matmul(kcur, vcur);
+        __builtin_amdgcn_s_setprio(0);
+        if (grp == 1) __builtin_amdgcn_s_waitcnt(0);   // set t + 2 (issued by B in SM(t))
+        fa_lds_barrier();
     };
 
     if (n_tiles > 0) {
-        gload_k(kr.begin);
-        gload_v(kr.begin);
-        store_k(0);
-        store_v(0);
-        gload_k(kr.begin + 1);
-        store_k(1);
-        __syncthreads();
-        qk(0, sA);
-        __syncthreads();   // K buffer 0 is refilled in the first step
-        using yes = std::integral_constant<bool, true>;
-        using no = std::integral_constant<bool, false>;
-        int it = 0;
-        for (; it + 2 < n_tiles; it += 2) {
-            step(yes{}, it, sA, sB);
-            step(yes{}, it + 1, sB, sA);
-        }
-        if (it + 1 < n_tiles) {
-            step(yes{}, it, sA, sB);
-            step(no{}, it + 1, sB, sA);
+        using one = std::integral_constant<int, 1>;
+        using zero = std::integral_constant<int, 0>;
+        dload(kp, kr.begin, lds_k0);                         // set 0
+        dload(vp, kr.begin, lds_v1);                         // set 1
+        if (n_tiles > 1) dload(kp, kr.begin + 1, lds_k1);
+        __builtin_amdgcn_s_waitcnt(0);
+        fa_lds_barrier();
+        if (grp == 0) {
+            qk(lds_k0);
+            fa_lds_barrier();
         } else {
-            step(no{}, it, sA, sB);
+            fa_lds_barrier();
+            qk(lds_k0);
+            fa_lds_barrier();
         }
+        int t = 0;
+        for (; t + 1 < n_tiles; t += 2) {
+            iter(one{}, t);
+            iter(zero{}, t + 1);
+        }
+        if (t < n_tiles) iter(one{}, t);
     }
 
     // Epilogue: O = O / l, LSE = ln2 (m + log2 l); rows with nothing visible give 0 and -inf.
+    const float l_tot = pair_sum(l_run);
+    if (row_ok) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (hl == 0) {
+            a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + row] =
+                l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        }
+        uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.q_bs + h * a.q_hs +
+                       (int64_t(g.q_start) + row) * a.q_rs;
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-        const float l_tot = pair_sum(l_run[gi]);
-        if (row_ok[gi]) {
-            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            if (hl == 0) {
-                a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + row[gi]] =
-                    l_tot > 0.f ? (m_run[gi] + log2f(l_tot)) * kLn2 : -INFINITY;
-            }
-            uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.q_bs + h * a.q_hs +
-                           (int64_t(g.q_start) + row[gi]) * a.q_rs;
+        for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int d = 32 * db + 8 * q4 + 4 * hl;
-                    const u32x2 w = {io::pack(oacc[gi][db][4 * q4 + 0] * inv, oacc[gi][db][4 * q4 + 1] * inv),
-                                     io::pack(oacc[gi][db][4 * q4 + 2] * inv, oacc[gi][db][4 * q4 + 3] * inv)};
-                    *reinterpret_cast<u32x2*>(op + d) = w;
-                }
+            for (int gi = 0; gi < 4; ++gi) {
+                const int d = 32 * db + 8 * gi + 4 * hl;
+                const u32x2 w = {io::pack(oacc[db][4 * gi + 0] * inv, oacc[db][4 * gi + 1] * inv),
+                                 io::pack(oacc[db][4 * gi + 2] * inv, oacc[db][4 * gi + 3] * inv)};
+                *reinterpret_cast<u32x2*>(op + d) = w;
             }
         }
     }
+    // Group A ran one phase ahead: its last barrier matches B's final MM phase.
+    if (n_tiles > 0 && grp == 0) fa_lds_barrier();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1042,14 +1050,14 @@ void launch_mfma32_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipSt
 }
 
 template <int D, bool BF>
-void launch_mfma64_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipStream_t s) {
-    const dim3 block(W64_THREADS);
+void launch_pp_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipStream_t s) {
+    const dim3 block(PP_THREADS);
     if (alibi) {
-        if (dense) fa_fwd_mfma64<D, BF, true, true, W64_BN><<<grid, block, 0, s>>>(a);
-        else fa_fwd_mfma64<D, BF, true, false, W64_BN><<<grid, block, 0, s>>>(a);
+        if (dense) fa_fwd_pp<D, BF, true, true><<<grid, block, 0, s>>>(a);
+        else fa_fwd_pp<D, BF, true, false><<<grid, block, 0, s>>>(a);
     } else {
-        if (dense) fa_fwd_mfma64<D, BF, false, true, W64_BN><<<grid, block, 0, s>>>(a);
-        else fa_fwd_mfma64<D, BF, false, false, W64_BN><<<grid, block, 0, s>>>(a);
+        if (dense) fa_fwd_pp<D, BF, false, true><<<grid, block, 0, s>>>(a);
+        else fa_fwd_pp<D, BF, false, false><<<grid, block, 0, s>>>(a);
     }
 }
 
@@ -1102,7 +1110,7 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
         std::fprintf(stderr,
                      "[fa] kernel=%s bm=%d bn=%d items/head=%lld blocks=%lld kv tiles visited/full/"
                      "dense=%lld/%lld/%lld table=%d reverse=%d xcd_major=%d ws=%zu\n",
-                     p.kernel == FA_KERNEL_MFMA ? "mfma64" : (p.kernel == FA_KERNEL_MFMA32 ? "mfma32" : "generic"),
+                     p.kernel == FA_KERNEL_PP ? "pingpong" : (p.kernel == FA_KERNEL_MFMA32 ? "mfma32" : "generic"),
                      p.bm, p.bn,
                      (long long)p.n_items, (long long)nblocks, (long long)p.kv_tiles_visited,
                      (long long)p.kv_tiles_full, (long long)p.kv_tiles_total, int(p.table),
@@ -1115,14 +1123,14 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     const bool alibi = alibi_slopes != nullptr;
     const bool dense = sparse_mode == 1;
     (void)hipGetLastError();
-    if (p.kernel == FA_KERNEL_MFMA) {
+    if (p.kernel == FA_KERNEL_PP) {
         const bool bf = dims->dtype == FA_DTYPE_BF16;
         if (p.D == 128) {
-            if (bf) launch_mfma64_d<128, true>(a, alibi, dense, grid, s);
-            else launch_mfma64_d<128, false>(a, alibi, dense, grid, s);
+            if (bf) launch_pp_d<128, true>(a, alibi, dense, grid, s);
+            else launch_pp_d<128, false>(a, alibi, dense, grid, s);
         } else {
-            if (bf) launch_mfma64_d<64, true>(a, alibi, dense, grid, s);
-            else launch_mfma64_d<64, false>(a, alibi, dense, grid, s);
+            if (bf) launch_pp_d<64, true>(a, alibi, dense, grid, s);
+            else launch_pp_d<64, false>(a, alibi, dense, grid, s);
         }
     } else if (p.kernel == FA_KERNEL_MFMA32) {
         const bool bf = dims->dtype == FA_DTYPE_BF16;

@@ -33,10 +33,11 @@ bool mfma_eligible(int32_t dtype, int64_t N, int64_t D) {
            N * D * 2 * 256 < (int64_t(1) << 31);
 }
 
-// FA_KERNEL=mfma64 selects the 64-rows-per-wave MFMA kernel (kept for comparisons).
-bool prefer_mfma64() {
+// FA_KERNEL=mfma32 selects the 4-wave MFMA kernel instead of the ping-pong one (for
+// comparisons).
+bool prefer_mfma32() {
     const char* e = std::getenv("FA_KERNEL");
-    return e && std::strcmp(e, "mfma64") == 0;
+    return e && std::strcmp(e, "mfma32") == 0;
 }
 
 }  // namespace
@@ -154,10 +155,10 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     p.bm = FA_GEN_BM;
     p.bn = FA_GEN_BN;
     if (mfma_eligible(d.dtype, d.N, d.D)) {
-        if (prefer_mfma64()) {
-            p.kernel = FA_KERNEL_MFMA;
-            p.bm = FA_MFMA_BM;
-            p.bn = FA_MFMA_BN;
+        if (!prefer_mfma32()) {
+            p.kernel = FA_KERNEL_PP;
+            p.bm = FA_PP_BM;
+            p.bn = FA_PP_BN;
         } else {
             p.kernel = FA_KERNEL_MFMA32;
             p.bm = FA_MFMA32_BM;

@@ -29,9 +29,9 @@ struct fa_call {
 };
 
 // Kernel families and their tiles.
-enum { FA_KERNEL_GENERIC = 0, FA_KERNEL_MFMA = 1, FA_KERNEL_MFMA32 = 2 };
-constexpr int FA_MFMA_BM = 256;     // 4 waves x 64 rows
-constexpr int FA_MFMA_BN = 32;
+enum { FA_KERNEL_GENERIC = 0, FA_KERNEL_PP = 1, FA_KERNEL_MFMA32 = 2 };
+constexpr int FA_PP_BM = 256;       // 8 waves x 32 rows, two groups in ping-pong
+constexpr int FA_PP_BN = 64;
 constexpr int FA_MFMA32_BM = 128;   // 4 waves x 32 rows
 constexpr int FA_MFMA32_BN = 64;
 constexpr int FA_GEN_BM = 64;

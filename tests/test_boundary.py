@@ -189,8 +189,8 @@ def test_workspace_size(lib):
     d = tnd([300, 7], [300, 9])
     n = fb.fa_fwd_workspace_size(d, "TND", 3, [300, 307], [300, 309])
     bm, bn, nq, nk = fb.fa_tile_shape(d, "TND", [300, 307], [300, 309])
-    assert (bm, bn) == (128, 64)
-    assert nq == 3 + 1 and nk == 5
+    assert (bm, bn) == (256, 64)
+    assert nq == 2 + 1 and nk == 5
     assert n >= 2 * 32 + nq * 8
     d32 = tnd([300, 7], [300, 9], dtype=0, D=16)
     bm, bn, nq, nk = fb.fa_tile_shape(d32, "TND", [300, 307], [300, 309])
