@@ -548,6 +548,21 @@ __device__ __forceinline__ void fa_lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Phase barrier that lets this wave's last N LDS reads stay in flight (LDS operations complete
+// in order, so everything issued before them has completed). For reads of data that no other
+// wave overwrites before the next barrier.
+template <int N>
+__device__ __forceinline__ void fa_lds_barrier_pending() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));   // lgkmcnt(N); vmcnt and expcnt left alone
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediate for vmcnt(n) alone (n < 16).
+constexpr int fa_vmcnt(int n) { return 0x0F70 | n; }
+
 template <int D, bool IS_BF16, bool ALIBI, bool DENSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(PP_THREADS, PP_THREADS),
                           amdgpu_waves_per_eu(2, 2))) void
@@ -560,10 +575,11 @@ fa_fwd_pp(const fa_kargs a) {
     constexpr int DBLK = D / 32;                 // 32-row blocks of O^T
     constexpr int TILE_CHUNKS = BN * KCH;        // 16-byte chunks per K or V tile
     constexpr int LOADS = TILE_CHUNKS / NT;      // direct loads per thread and tile
+    constexpr int BATCH = 2 * LOADS;             // loads per thread and set (V and K)
     static_assert(LOADS >= 1 && LOADS <= 2 && TILE_CHUNKS % NT == 0, "tile shape");
 
-    __shared__ u32x4 lds_k0[TILE_CHUNKS], lds_k1[TILE_CHUNKS];
-    __shared__ u32x4 lds_v0[TILE_CHUNKS], lds_v1[TILE_CHUNKS];
+    __shared__ u32x4 lds_k0[TILE_CHUNKS], lds_k1[TILE_CHUNKS], lds_k2[TILE_CHUNKS], lds_k3[TILE_CHUNKS];
+    __shared__ u32x4 lds_v0[TILE_CHUNKS], lds_v1[TILE_CHUNKS], lds_v2[TILE_CHUNKS], lds_v3[TILE_CHUNKS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -750,26 +766,35 @@ fa_fwd_pp(const fa_kargs a) {
         asm volatile("" : : "v"(l_run));
     };
 
-    // MM(t): O^T += V^T P^T from set buffer (vb), then S^T of the next tile from (kb). After
+    // The V^T operands of the first NPRE PV MFMAs are read at the end of the preceding softmax
+    // phase, so a matrix phase starts with MFMAs instead of waiting for LDS.
+    constexpr int NPRE = DBLK;   // (t = 0, db = 0 .. DBLK-1)
+    u32x4 vpre[NPRE];
+    auto vread = [&](const char* vbase, int t, int db) __attribute__((always_inline)) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vbase + v_off[0][db] + t * 16 * KCH * 16));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vbase + v_off[1][db] + t * 16 * KCH * 16));
+        return u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                     __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+    };
+    auto prefetch = [&](const u32x4* vb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < NPRE; ++db) vpre[db] = vread(reinterpret_cast<const char*>(vb), 0, db);
+    };
+    // MM(t): O^T += V^T P^T from V buffer vb, then S^T of the next tile from K buffer kb. After
     // the last tile the S^T product reads a stale K buffer and its result is never used.
-    auto matmul = [&](const u32x4* kb, const u32x4* vb) __attribute__((always_inline)) {
+    auto matmul = [&](const u32x4* kb, const u32x4* vb, auto&& between) __attribute__((always_inline)) {
         const char* vbase = reinterpret_cast<const char*>(vb);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(vbase + v_off[0][db] + t * 16 * KCH * 16));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(vbase + v_off[1][db] + t * 16 * KCH * 16));
-                const u32x4 vop = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                                   __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-                oacc[db] = io::mma(vop, pop[t], oacc[db]);
-            }
-        }
+            for (int db = 0; db < DBLK; ++db)
+                oacc[db] = io::mma(t == 0 ? vpre[db] : vread(vbase, t, db), pop[t], oacc[db]);
+        between();
         qk(kb);
-        // LDS reads run about three MFMAs ahead: six reads up front, then two per PV MFMA
-        // (its two V^T halves) and one per S^T MFMA.
+        // LDS reads run about three MFMAs ahead: two per PV MFMA (its two V^T halves) and one
+        // per S^T MFMA.
         constexpr int NPV = 4 * DBLK, NQK = 2 * KSTEPS;
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
@@ -780,53 +805,76 @@ fa_fwd_pp(const fa_kargs a) {
         }
     };
 
-    // Loads of set t + 2 = {K(t+2), V(t+1)} (the parts that exist) into the free buffer.
-    auto issue = [&](int t, u32x4* kfill, u32x4* vfill) __attribute__((always_inline)) {
-        if (t + 1 < n_tiles) dload(vp, kr.begin + t + 1, vfill);
-        if (t + 2 < n_tiles) dload(kp, kr.begin + t + 2, kfill);
-    };
-
-    // Iteration t: SM(t) then MM(t); set t + 1 sits in buffer PB.
-    auto iter = [&](auto pb_tag, int t) __attribute__((always_inline)) {
-        constexpr int PB = decltype(pb_tag)::value;
-        const u32x4* kcur = PB ? lds_k1 : lds_k0;
-        const u32x4* vcur = PB ? lds_v1 : lds_v0;
-        u32x4* kfill = PB ? lds_k0 : lds_k1;
-        u32x4* vfill = PB ? lds_v0 : lds_v1;
-        if (grp == 1) issue(t, kfill, vfill);
+    // Set u = {V(u), K(u+1)} is what MM(u) reads; it lives in buffer u % 4. Both groups issue
+    // their share of set t + 3 during MM(t) (into the buffer of set t - 1, which MM(t-1) of both
+    // groups has finished with) and wait at the end of MM(t) until only the newest batch is in
+    // flight. For group A that phase is slot 2t+2, for B slot 2t+3; set u is first read by A's
+    // prefetch in slot 2u+1, after both waits (slots 2u-2 and 2u-1) and their barriers, giving
+    // each batch three phases to land. Every batch is the same number of loads per thread (an
+    // empty range past the last tile: nothing read, zeros written to the free buffer), and both
+    // groups issue and wait at the same points of the program.
+    auto iter = [&](auto s_tag, int t) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_tag)::value;   // t % 4
+        constexpr int F = (S + 3) % 4;              // buffer of set t + 3 (and of set t - 1)
+        const u32x4* k_cur = S == 0 ? lds_k0 : (S == 1 ? lds_k1 : (S == 2 ? lds_k2 : lds_k3));
+        const u32x4* v_cur = S == 0 ? lds_v0 : (S == 1 ? lds_v1 : (S == 2 ? lds_v2 : lds_v3));
+        u32x4* k_fill = F == 0 ? lds_k0 : (F == 1 ? lds_k1 : (F == 2 ? lds_k2 : lds_k3));
+        u32x4* v_fill = F == 0 ? lds_v0 : (F == 1 ? lds_v1 : (F == 2 ? lds_v2 : lds_v3));
         softmax(t);
-        if (grp == 0) __builtin_amdgcn_s_waitcnt(0);   // set t + 1 (issued by A in MM(t-1))
-        fa_lds_barrier();
-        if (grp == 0) issue(t, kfill, vfill);
+        prefetch(v_cur);
+        fa_lds_barrier_pending<2 * NPRE>();   // the prefetched V^T reads may still be in flight
         __builtin_amdgcn_s_setprio(1);
-        matmul(kcur, vcur);
+        matmul(k_cur, v_cur, [&]() __attribute__((always_inline)) {
+            dload(vp, kr.begin + t + 3, v_fill);
+            dload(kp, kr.begin + t + 4, k_fill);
+        });
         __builtin_amdgcn_s_setprio(0);
-        if (grp == 1) __builtin_amdgcn_s_waitcnt(0);   // set t + 2 (issued by B in SM(t))
+        __builtin_amdgcn_s_waitcnt(fa_vmcnt(BATCH));
         fa_lds_barrier();
     };
 
     if (n_tiles > 0) {
-        using one = std::integral_constant<int, 1>;
-        using zero = std::integral_constant<int, 0>;
-        dload(kp, kr.begin, lds_k0);                         // set 0
-        dload(vp, kr.begin, lds_v1);                         // set 1
-        if (n_tiles > 1) dload(kp, kr.begin + 1, lds_k1);
+        // K(0) goes into buffer 3's K half (set 3 is not loaded before iteration 0's matrix
+        // phase, after both groups have used K(0)); sets 0, 1, 2 into buffers 0, 1, 2.
+        dload(kp, kr.begin, lds_k3);
+        dload(vp, kr.begin, lds_v0);
+        dload(kp, kr.begin + 1, lds_k0);
+        dload(vp, kr.begin + 1, lds_v1);
+        dload(kp, kr.begin + 2, lds_k1);
+        dload(vp, kr.begin + 2, lds_v2);
+        dload(kp, kr.begin + 3, lds_k2);
         __builtin_amdgcn_s_waitcnt(0);
         fa_lds_barrier();
         if (grp == 0) {
-            qk(lds_k0);
+            qk(lds_k3);
             fa_lds_barrier();
         } else {
             fa_lds_barrier();
-            qk(lds_k0);
+            qk(lds_k3);
             fa_lds_barrier();
         }
+        using s0 = std::integral_constant<int, 0>;
+        using s1 = std::integral_constant<int, 1>;
+        using s2 = std::integral_constant<int, 2>;
+        using s3 = std::integral_constant<int, 3>;
+        // Full trips of four, then a tail with nested guards: every path into an iteration runs
+        // the earlier iterations (and their waits), which the compiler's own wait analysis must
+        // be able to see.
         int t = 0;
-        for (; t + 1 < n_tiles; t += 2) {
-            iter(one{}, t);
-            iter(zero{}, t + 1);
+        for (; t + 4 <= n_tiles; t += 4) {
+            iter(s0{}, t);
+            iter(s1{}, t + 1);
+            iter(s2{}, t + 2);
+            iter(s3{}, t + 3);
         }
-        if (t < n_tiles) iter(one{}, t);
+        if (t < n_tiles) {
+            iter(s0{}, t);
+            if (t + 1 < n_tiles) {
+                iter(s1{}, t + 1);
+                if (t + 2 < n_tiles) iter(s2{}, t + 2);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
     }
 
     // Epilogue: O = O / l, LSE = ln2 (m + log2 l); rows with nothing visible give 0 and -inf.
