@@ -30,7 +30,9 @@ Readings taken where the pages are silent or garbled (all listed in the design n
   from the bottom-right corner (j - i - (Skv - Sq)).
 - both band bounds are inclusive.
 - a row whose every key is masked yields O = 0 and LSE = -inf.
-- the alibi bias is slope_h * (j - i - (Skv - Sq)), added after scaling.
+- the alibi bias is added after scaling. Right-aligned: slope_h * (j - i - (Skv - Sq));
+  the square-root variant takes the square root of that bias's magnitude (sign kept);
+  left-aligned: slope_h * (j - i). The page's figures with the exact values are missing.
 - modes 5 and 6: columns j < prefix_b are visible in addition to right-down causal.
 - modes 7 and 8: the band batch is the last (7) or first (8) batch with Sq_b > 0 and
   Skv_b > 0.
@@ -155,14 +157,32 @@ def count_visible_loops(sparse_mode: int, sq: int, skv: int, *, pre_tokens: int 
 
 
 # ----------------------------------------------------------------------------------------
-# Alibi bias ("压缩mask", alibi scenario: slope x relative-position bias, right-aligned).
+# Alibi bias ("压缩mask", section "不同压缩mask的构造方法", alibi scenario: a per-head
+# slope times a relative-position bias, in three variants).
 # ----------------------------------------------------------------------------------------
 
-def alibi_bias(slope: float, i, j, sq: int, skv: int) -> np.ndarray:
-    """slope * (j - i - (Skv - Sq)): zero on the bottom-right diagonal, linear in distance."""
+ALIBI_MODES = ("right", "sqrt", "left")
+
+
+def alibi_bias(slope: float, i, j, sq: int, skv: int, mode: str = "right") -> np.ndarray:
+    """Alibi bias of query row i and key j (batch-local indices).
+
+    With d = i + (Skv - Sq) - j, the distance from the bottom-right diagonal:
+    - "right" (right-aligned bias): slope * (j - i - (Skv - Sq)) = -slope * d;
+    - "sqrt" (the right-aligned bias with its magnitude square-rooted):
+      -slope * sign(d) * sqrt(|d|);
+    - "left" (left-aligned bias, measured from the top-left diagonal): slope * (j - i).
+    """
     i = np.asarray(i, dtype=np.float64)
     j = np.asarray(j, dtype=np.float64)
-    return float(slope) * (j - i - float(skv - sq))
+    if mode == "left":
+        return float(slope) * (j - i)
+    d = i + float(skv - sq) - j
+    if mode == "right":
+        return -float(slope) * d
+    if mode == "sqrt":
+        return -float(slope) * np.sign(d) * np.sqrt(np.abs(d))
+    raise ValueError(mode)
 
 
 # ----------------------------------------------------------------------------------------
@@ -238,14 +258,15 @@ def _mask_rows(atten_mask, b, h, rows, skv):
 
 def attention(q, k, v, *, layout: str = "BNSD", sparse_mode: int = 0, scale: float,
               pre_tokens: int = 0, next_tokens: int = 0, actual_seq_qlen=None,
-              actual_seq_kvlen=None, prefix=None, alibi_slopes=None, atten_mask=None):
+              actual_seq_kvlen=None, prefix=None, alibi_slopes=None, atten_mask=None,
+              alibi_mode: str = "right"):
     """Full forward pass in fp64. Returns (out, lse).
 
     Layouts: BNSD q [B, N, Sq, D]; BSND q [B, Sq, N, D]; TND q [T_q, N, D] with the
     cumulative ``actual_seq_qlen`` / ``actual_seq_kvlen``. ``out`` has q's layout; ``lse``
     is [B, N, Sq] (BNSD, BSND) or [N, T_q] (TND). ``atten_mask`` (mode 1) is
     [B or 1, N or 1, Sq, Skv], non-zero = masked. ``prefix`` (modes 5, 6) has one entry per
-    batch. ``alibi_slopes`` has one slope per head.
+    batch. ``alibi_slopes`` has one slope per head; ``alibi_mode`` is one of ALIBI_MODES.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -271,7 +292,8 @@ def attention(q, k, v, *, layout: str = "BNSD", sparse_mode: int = 0, scale: flo
                 (ql, kl))
             bias = None
             if alibi_slopes is not None:
-                bias = alibi_bias(alibi_slopes[h], rows[:, None], np.arange(kl)[None, :], ql, kl)
+                bias = alibi_bias(alibi_slopes[h], rows[:, None], np.arange(kl)[None, :], ql, kl,
+                                  alibi_mode)
             qh = _head_view(q, layout, b, h, qs, ql)
             kh = _head_view(k, layout, b, h, ks, kl)
             vh = _head_view(v, layout, b, h, ks, kl)
@@ -291,7 +313,7 @@ def attention(q, k, v, *, layout: str = "BNSD", sparse_mode: int = 0, scale: flo
 def attention_rows(q, k, v, rows: Iterable, *, layout: str = "BNSD", sparse_mode: int = 0,
                    scale: float, pre_tokens: int = 0, next_tokens: int = 0,
                    actual_seq_qlen=None, actual_seq_kvlen=None, prefix=None,
-                   alibi_slopes=None, atten_mask=None):
+                   alibi_slopes=None, atten_mask=None, alibi_mode: str = "right"):
     """The same definition evaluated only for selected rows ``(b, h, i)`` (i batch-local).
 
     Used at sizes where a full Sq x Skv matrix per head would take too long. Returns
@@ -315,7 +337,8 @@ def attention_rows(q, k, v, rows: Iterable, *, layout: str = "BNSD", sparse_mode
             visible(sparse_mode, ii[:, None], np.arange(kl)[None, :], ql, kl, **kw), (1, kl))
         bias = None
         if alibi_slopes is not None:
-            bias = alibi_bias(alibi_slopes[h], ii[:, None], np.arange(kl)[None, :], ql, kl)
+            bias = alibi_bias(alibi_slopes[h], ii[:, None], np.arange(kl)[None, :], ql, kl,
+                              alibi_mode)
         qh = np.asarray(_head_view(q, layout, b, h, qs, ql)[i:i + 1], dtype=np.float64)
         kh = np.asarray(_head_view(k, layout, b, h, ks, kl), dtype=np.float64)
         vh = np.asarray(_head_view(v, layout, b, h, ks, kl), dtype=np.float64)

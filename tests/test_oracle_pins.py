@@ -357,6 +357,79 @@ def test_alibi_left_vs_right_alignment_shift():
     np.testing.assert_allclose(l_l - l_r, slope * (skv - sq), atol=1e-13)
 
 
+def test_alibi_left_mode_is_a_row_shift_of_right():
+    """"压缩mask", alibi scenario, left-aligned vs right-aligned bias: per row the two differ
+    by the constant slope * (Skv - Sq), so O is the same and LSE moves by that constant,
+    per head, whatever the mask (modes 3 and 5, Sq != Skv)."""
+    rng = np.random.default_rng(41)
+    B, N, sq, skv, d = 2, 3, 6, 11, 8
+    q, k, v = (rng.standard_normal((B, N, n, d)) for n in (sq, skv, skv))
+    slopes = [0.5, 0.25, 0.125]
+    for mode, extra in ((3, {}), (5, {"prefix": [9, 2]})):
+        o_r, l_r = oracle.attention(q, k, v, sparse_mode=mode, scale=0.3, alibi_slopes=slopes, **extra)
+        o_l, l_l = oracle.attention(q, k, v, sparse_mode=mode, scale=0.3, alibi_slopes=slopes,
+                                    alibi_mode="left", **extra)
+        np.testing.assert_allclose(o_l, o_r, atol=1e-13)
+        for h, sl in enumerate(slopes):
+            np.testing.assert_allclose(l_l[:, h] - l_r[:, h], sl * (skv - sq), atol=1e-12)
+
+
+def _one_hot_probe(sq, skv, mode, slope, alibi_mode, **kw):
+    """q = 0 and v = identity: O_i is the row's softmax weight vector, LSE_i its log-sum."""
+    q = np.zeros((1, 1, sq, 4))
+    k = np.ones((1, 1, skv, 4))
+    v = np.eye(skv)[None, None]
+    return oracle.attention(q, k, v, sparse_mode=mode, scale=1.0, alibi_slopes=[slope],
+                            alibi_mode=alibi_mode, **kw)
+
+
+def test_alibi_sqrt_closed_form_causal():
+    """"压缩mask", alibi scenario, square-root right-aligned bias: with q = 0 the score of key
+    j in right-down causal row i is -slope * sqrt(d), d = i + (Skv - Sq) - j >= 0, so
+    LSE_i = ln sum_{d=0}^{i+off} exp(-slope sqrt(d)) and the weights are exp(-slope sqrt(d) - LSE_i)
+    (closed form evaluated here with math.fsum)."""
+    sq, skv, slope = 5, 9, 0.7
+    off = skv - sq
+    o, lse = _one_hot_probe(sq, skv, 3, slope, "sqrt")
+    for i in range(sq):
+        ds = [i + off - j for j in range(i + off + 1)]
+        ref_lse = math.log(math.fsum(math.exp(-slope * math.sqrt(dd)) for dd in ds))
+        assert abs(lse[0, 0, i] - ref_lse) < 1e-12
+        for j in range(skv):
+            w = math.exp(-slope * math.sqrt(i + off - j) - ref_lse) if j <= i + off else 0.0
+            assert abs(o[0, 0, i, j] - w) < 1e-12
+
+
+def test_alibi_sqrt_above_diagonal_sign():
+    """Keys right of the bottom-right diagonal (visible in a mode-4 band with next > 0) get the
+    positive bias slope * sqrt(j - i - off): the reading that keeps the right-aligned bias's
+    sign and square-roots its magnitude."""
+    sq, skv, slope = 4, 6, 0.5
+    off = skv - sq
+    o, lse = _one_hot_probe(sq, skv, 4, slope, "sqrt", pre_tokens=1, next_tokens=2)
+    above = 0
+    for i in range(sq):
+        js = [j for j in range(skv) if -1 <= j - i - off <= 2]
+        sc = {j: -slope * math.copysign(math.sqrt(abs(i + off - j)), i + off - j) for j in js}
+        ref_lse = math.log(math.fsum(math.exp(x) for x in sc.values()))
+        assert abs(lse[0, 0, i] - ref_lse) < 1e-12
+        for j in js:
+            assert abs(o[0, 0, i, j] - math.exp(sc[j] - ref_lse)) < 1e-12
+        above += sum(j > i + off for j in js)
+    assert above > 0
+
+
+def test_alibi_zero_slope_is_no_bias():
+    """A zero slope leaves every variant equal to attention without alibi."""
+    rng = np.random.default_rng(43)
+    q, k, v = (rng.standard_normal((1, 2, n, 8)) for n in (5, 7, 7))
+    o0, l0 = oracle.attention(q, k, v, sparse_mode=3, scale=0.4)
+    for m in oracle.ALIBI_MODES:
+        o, l = oracle.attention(q, k, v, sparse_mode=3, scale=0.4, alibi_slopes=[0.0, 0.0], alibi_mode=m)
+        np.testing.assert_allclose(o, o0, atol=1e-14)
+        np.testing.assert_allclose(l, l0, atol=1e-14)
+
+
 # ---------------------------------------------------------------------------------------
 # Layouts
 # ---------------------------------------------------------------------------------------
