@@ -6,6 +6,7 @@ product.
 """
 
 from .attention import (  # noqa: F401
+    ALIBI_MODES,
     alibi_bias,
     attention,
     attention_head,
