@@ -131,6 +131,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="causal_8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--alibi-mode", default="right", choices=["right", "sqrt", "left"],
+                    help="alibi variant for workloads with alibi")
     ap.add_argument("--cpu-heads", type=int, default=48,
                     help="(batch, head) slices of the workload the CPU oracle is timed on")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -166,7 +168,8 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     kw = dict(layout=w.layout, sparse_mode=w.sparse_mode, pre_tokens=w.pre_tokens, next_tokens=w.next_tokens,
               actual_seq_qlen=w.actual_seq_qlen, actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix,
-              alibi_slopes=slopes, scale=w.softmax_scale, workspace=ws if ws_bytes else None)
+              alibi_slopes=slopes, alibi_mode=args.alibi_mode, scale=w.softmax_scale,
+              workspace=ws if ws_bytes else None)
     pairs = visible_pairs(w, dev)
     flops = 4 * w.D * pairs
     elem = q.element_size()
@@ -205,7 +208,8 @@ def main():
         "config": {"workload": args.workload, "layout": w.layout, "sparse_mode": w.sparse_mode,
                    "B": w.B, "N": w.N, "Sq": w.Sq, "Skv": w.Skv, "D": w.D,
                    "pre_tokens": w.pre_tokens, "next_tokens": w.next_tokens,
-                   "alibi": w.alibi, "visible_pairs": pairs, "flop_per_step": flops},
+                   "alibi": (args.alibi_mode if w.alibi else False), "visible_pairs": pairs,
+                   "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,

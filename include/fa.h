@@ -54,6 +54,17 @@ typedef int32_t fa_status;
 #define FA_LAYOUT_BSND 1
 #define FA_LAYOUT_TND 2
 
+/* Alibi bias variants ("压缩mask", section "不同压缩mask的构造方法", alibi scenario). With
+ * d = i - j + (Skv_b - Sq_b), the distance of key j from query i's bottom-right diagonal:
+ *   FA_ALIBI_RIGHT: bias_ij = slope_h * (j - i - (Skv_b - Sq_b)) = -slope_h * d (right-aligned);
+ *   FA_ALIBI_SQRT:  bias_ij = -slope_h * sign(d) * sqrt(|d|) (the right-aligned bias with its
+ *                   magnitude square-rooted);
+ *   FA_ALIBI_LEFT:  bias_ij = slope_h * (j - i) (left-aligned: zero on the top-left diagonal).
+ * The page's figures with the exact values did not survive; these are the plain readings. */
+#define FA_ALIBI_RIGHT 0
+#define FA_ALIBI_SQRT 1
+#define FA_ALIBI_LEFT 2
+
 /* Element types of q, k, v and out (all four share one). softmax_lse is always fp32. */
 #define FA_DTYPE_F32 0
 #define FA_DTYPE_F16 1
@@ -101,8 +112,10 @@ fa_status fa_fwd_workspace_size(const fa_dims* dims, int32_t layout, int32_t spa
  *   q, k, v, out:  device, dims->dtype, in `layout`.
  *   softmax_lse:   device fp32, [B, N, Sq] (BNSD/BSND) or [N, T_q] (TND); natural log of the
  *                  sum over visible j of exp(scale * q_i.k_j + bias_ij).
- *   alibi_slopes:  device fp32 [N] or NULL. When given, bias_ij = slope_h * (j - i - (Skv_b - Sq_b))
- *                  ("压缩mask", alibi scenario, right-aligned); D <= 128; not with modes 7/8.
+ *   alibi_slopes:  device fp32 [N] or NULL. When given, the bias of head h is slope_h times
+ *                  the relative-position term alibi_mode selects; D <= 128; not with modes 7/8.
+ *   alibi_mode:    FA_ALIBI_RIGHT, FA_ALIBI_SQRT or FA_ALIBI_LEFT (else FA_ERR_PARAM_INVALID);
+ *                  checked even when alibi_slopes is NULL.
  *   scale:         softmax scale, finite and > 0 (e.g. 1/sqrt(D)).
  *   workspace:     device, at least fa_fwd_workspace_size bytes (may be NULL when that is 0).
  * Supported: D <= 128 for every dtype; the MFMA kernels serve fp16/bf16 with D = 64 or 128,
@@ -111,7 +124,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  const fa_dims* dims, int32_t layout, int32_t sparse_mode,
                  int64_t pre_tokens, int64_t next_tokens,
                  const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
-                 const int64_t* prefix, const float* alibi_slopes,
+                 const int64_t* prefix, const float* alibi_slopes, int32_t alibi_mode,
                  const uint8_t* atten_mask, const int64_t* mask_bcast,
                  float scale, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -62,7 +62,7 @@ def load_library():
     lib.fa_fwd_workspace_size.argtypes = [pdims, i32, i32, pi64, pi64, ctypes.POINTER(sz)]
     lib.fa_fwd_workspace_size.restype = i32
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
-                           vp, vp, pi64, ctypes.c_float, vp, sz, vp]
+                           vp, i32, vp, pi64, ctypes.c_float, vp, sz, vp]
     lib.fa_fwd.restype = i32
     lib.fa_mask_probe.argtypes = [pdims, i32, i32, i64, i64, pi64, pi64, pi64, vp, pi64, vp, vp,
                                   vp, sz, vp]
@@ -149,10 +149,12 @@ def fa_fwd_workspace_size(dims: FaDims, layout, sparse_mode: int, actual_seq_qle
 
 def fa_fwd(q, k, v, out, softmax_lse, *, layout="BNSD", sparse_mode: int = 0, pre_tokens: int = 0,
            next_tokens: int = 0, actual_seq_qlen=None, actual_seq_kvlen=None, prefix=None,
-           alibi_slopes: Optional[torch.Tensor] = None, atten_mask: Optional[torch.Tensor] = None,
-           mask_bcast=None, scale: float, workspace: Optional[torch.Tensor] = None,
-           stream=None) -> None:
-    """Calls fa_fwd on device tensors. Raises FaError on a non-zero status."""
+           alibi_slopes: Optional[torch.Tensor] = None, alibi_mode="right",
+           atten_mask: Optional[torch.Tensor] = None, mask_bcast=None, scale: float,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Calls fa_fwd on device tensors. Raises FaError on a non-zero status.
+
+    alibi_mode: "right", "sqrt" or "left" (or the FA_ALIBI_* code)."""
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         _check_device_tensor(name, t, q.dtype)
@@ -167,10 +169,21 @@ def fa_fwd(q, k, v, out, softmax_lse, *, layout="BNSD", sparse_mode: int = 0, pr
     st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_lse), ctypes.byref(dims),
                     _layout_code(layout), int(sparse_mode), int(pre_tokens), int(next_tokens),
                     _i64(actual_seq_qlen), _i64(actual_seq_kvlen), _i64(prefix), _ptr(alibi_slopes),
-                    _ptr(atten_mask), _i64(mask_bcast), float(scale), _ptr(workspace), ws_bytes,
+                    _alibi_code(alibi_mode), _ptr(atten_mask), _i64(mask_bcast), float(scale), _ptr(workspace), ws_bytes,
                     stream if stream is not None else _stream(q.device))
     if st != 0:
         raise FaError(st, "fa_fwd")
+
+
+ALIBI_MODES = {"right": 0, "sqrt": 1, "left": 2}
+
+
+def _alibi_code(mode) -> int:
+    if isinstance(mode, str):
+        if mode not in ALIBI_MODES:
+            raise ValueError(f"alibi_mode must be one of {sorted(ALIBI_MODES)}")
+        return ALIBI_MODES[mode]
+    return int(mode)
 
 
 def lse_shape(q, layout, actual_seq_qlen=None):

@@ -60,6 +60,7 @@ struct fa_kargs {
     int32_t n_qtiles_fixed;
     int32_t reverse_qt;
     int32_t xcd_major;      // fixed-length launch order, see fa_decode_item
+    int32_t alibi_left;     // linear alibi measured from the top-left diagonal (else bottom-right)
     float scale_log2;       // scale * log2(e)
 };
 
@@ -210,11 +211,13 @@ constexpr int MF_THREADS = 256;
 // from the S^T accumulators; the V^T operand of O^T += V^T P^T is read from the row-major V
 // tile with ds_read_b64_tr_b16 (lane i of each 16-lane group receives element i%4 of the
 // chunks addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4), so no transpose pass is needed.
-template <int D, bool IS_BF16, bool ALIBI, bool DENSE>
+template <int D, bool IS_BF16, int AL, bool DENSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(MF_THREADS, MF_THREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 fa_fwd_mfma(const fa_kargs a) {
     static_assert(D == 64 || D == 128, "MFMA path covers D = 64 and 128");
+    static_assert(AL >= 0 && AL <= 2, "alibi kind: 0 none, 1 linear, 2 square root");
+    constexpr bool ALIBI = AL != 0;
     using io = mfma_io<IS_BF16>;
     constexpr int BM = MF_BM, BN = MF_BN, NT = MF_THREADS;
     constexpr int KCH = D / 8;                   // 16-byte chunks per K / V row
@@ -271,6 +274,7 @@ fa_fwd_mfma(const fa_kargs a) {
     float slope2 = 0.f;
     if (ALIBI) slope2 = a.slopes[h] * kLog2e;
     const int off = g.skv - g.sq;
+    const int aoff = a.alibi_left ? 0 : off;   // diagonal of the linear alibi bias
     const uint8_t* mrow = nullptr;
     if (DENSE) mrow = a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs;
 
@@ -380,13 +384,25 @@ fa_fwd_mfma(const fa_kargs a) {
             // Row maximum over this lane's 32 keys in four independent chains (short dependency
             // chains keep the VALU busy), then across the lane pair.
             float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            if (ALIBI) {
-                const float base = slope2 * float(j0 + 4 * hl - row - off);
+            if (AL == 1) {
+                const float base = slope2 * float(j0 + 4 * hl - row - aoff);
 #pragma unroll
                 for (int e = 0; e < 32; ++e) {
                     const int r = e & 15;
                     const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
                     s[e] = fmaf(s[e], sl2, fmaf(slope2, float(kc), base));
+                    m4[e & 3] = fmaxf(m4[e & 3], s[e]);
+                }
+            } else if (AL == 2) {
+                // Square-root bias: -slope sign(d) sqrt(|d|), d = i + (Skv - Sq) - j (v_sqrt_f32,
+                // within 1 ulp: d is an integer below 2^24).
+                const float dbase = float(row + off - j0 - 4 * hl);
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    const int r = e & 15;
+                    const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
+                    const float dd = dbase - float(kc);
+                    s[e] = fmaf(s[e], sl2, -slope2 * copysignf(__builtin_amdgcn_sqrtf(fabsf(dd)), dd));
                     m4[e & 3] = fmaxf(m4[e & 3], s[e]);
                 }
             } else {
@@ -563,11 +579,13 @@ __device__ __forceinline__ void fa_lds_barrier_pending() {
 // s_waitcnt immediate for vmcnt(n) alone (n < 16).
 constexpr int fa_vmcnt(int n) { return 0x0F70 | n; }
 
-template <int D, bool IS_BF16, bool ALIBI, bool DENSE>
+template <int D, bool IS_BF16, int AL, bool DENSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(PP_THREADS, PP_THREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 fa_fwd_pp(const fa_kargs a) {
     static_assert(D == 64 || D == 128, "MFMA path covers D = 64 and 128");
+    static_assert(AL >= 0 && AL <= 2, "alibi kind: 0 none, 1 linear, 2 square root");
+    constexpr bool ALIBI = AL != 0;
     using io = mfma_io<IS_BF16>;
     constexpr int BM = PP_BM, BN = PP_BN, NT = PP_THREADS;
     constexpr int KCH = D / 8;                   // 16-byte chunks per K / V row
@@ -626,6 +644,7 @@ fa_fwd_pp(const fa_kargs a) {
     // lgkmcnt(0), which also waits for every LDS read in flight.
     asm volatile("" : : "s"(sl2), "v"(slope2));
     const int off = g.skv - g.sq;
+    const int aoff = a.alibi_left ? 0 : off;   // diagonal of the linear alibi bias
     const uint8_t* mrow = nullptr;
     if (DENSE) mrow = a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs;
 
@@ -720,13 +739,25 @@ fa_fwd_pp(const fa_kargs a) {
 #pragma unroll
         for (int e = 0; e < 32; ++e) s[e] = sacc[e >> 4][e & 15];
         float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        if (ALIBI) {
-            const float base = slope2 * float(j0 + 4 * hl - row - off);
+        if (AL == 1) {
+            const float base = slope2 * float(j0 + 4 * hl - row - aoff);
 #pragma unroll
             for (int e = 0; e < 32; ++e) {
                 const int r = e & 15;
                 const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
                 s[e] = fmaf(s[e], sl2, fmaf(slope2, float(kc), base));
+                m4[e & 3] = fmaxf(m4[e & 3], s[e]);
+            }
+        } else if (AL == 2) {
+            // Square-root bias: -slope sign(d) sqrt(|d|), d = i + (Skv - Sq) - j (v_sqrt_f32,
+            // within 1 ulp: d is an integer below 2^24).
+            const float dbase = float(row + off - j0 - 4 * hl);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                const int r = e & 15;
+                const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
+                const float dd = dbase - float(kc);
+                s[e] = fmaf(s[e], sl2, -slope2 * copysignf(__builtin_amdgcn_sqrtf(fabsf(dd)), dd));
                 m4[e & 3] = fmaxf(m4[e & 3], s[e]);
             }
         } else {
@@ -920,6 +951,7 @@ constexpr int GN_BM = FA_GEN_BM;   // 64 query rows per workgroup (one wave)
 constexpr int GN_BN = FA_GEN_BN;   // 16 keys per tile
 
 template <typename T, int DMAX>
+// alibi: 0 none, 1 linear (right- or left-aligned per a.alibi_left), 2 square root.
 __global__ __launch_bounds__(GN_BM) void fa_fwd_generic(const fa_kargs a, int dense, int alibi) {
     // Q rows of this workgroup (padded by one float so each thread's row starts on its own
     // bank) and one K/V tile, all in fp32. Only the O accumulator lives in registers.
@@ -951,6 +983,7 @@ __global__ __launch_bounds__(GN_BM) void fa_fwd_generic(const fa_kargs a, int de
     const int row_lo = fa_row_lo(g, row), row_hi = fa_row_hi(g, row);
     const float slope2 = alibi ? a.slopes[h] * kLog2e : 0.f;
     const int off = g.skv - g.sq;
+    const int aoff = a.alibi_left ? 0 : off;   // diagonal of the linear alibi bias
     const uint8_t* mrow = dense ? a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs
                                 : nullptr;
     float m = -INFINITY, l = 0.f;
@@ -974,7 +1007,12 @@ __global__ __launch_bounds__(GN_BM) void fa_fwd_generic(const fa_kargs a, int de
             const int j = j0 + jj;
             const bool vis = dense ? (row_ok && j < g.skv && mrow[j] == 0) : (j >= row_lo && j <= row_hi);
             float sv = dot * a.scale_log2;
-            if (alibi) sv += slope2 * float(j - row - off);
+            if (alibi == 1) {
+                sv += slope2 * float(j - row - aoff);
+            } else if (alibi == 2) {
+                const float dd = float(row + off - j);   // square-root bias
+                sv -= slope2 * copysignf(__builtin_amdgcn_sqrtf(fabsf(dd)), dd);
+            }
             sv = vis ? sv : -INFINITY;
             const float m_new = fmaxf(m, sv);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -1086,31 +1124,33 @@ fa_status upload_tables(const fa_plan& p, void* workspace, hipStream_t stream) {
 }
 
 template <int D, bool BF>
-void launch_mfma32_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipStream_t s) {
+void launch_mfma32_d(const fa_kargs& a, int al, bool dense, dim3 grid, hipStream_t s) {
     const dim3 block(MF_THREADS);
-    if (alibi) {
-        if (dense) fa_fwd_mfma<D, BF, true, true><<<grid, block, 0, s>>>(a);
-        else fa_fwd_mfma<D, BF, true, false><<<grid, block, 0, s>>>(a);
-    } else {
-        if (dense) fa_fwd_mfma<D, BF, false, true><<<grid, block, 0, s>>>(a);
-        else fa_fwd_mfma<D, BF, false, false><<<grid, block, 0, s>>>(a);
+    switch (al * 2 + (dense ? 1 : 0)) {
+        case 0: fa_fwd_mfma<D, BF, 0, false><<<grid, block, 0, s>>>(a); break;
+        case 1: fa_fwd_mfma<D, BF, 0, true><<<grid, block, 0, s>>>(a); break;
+        case 2: fa_fwd_mfma<D, BF, 1, false><<<grid, block, 0, s>>>(a); break;
+        case 3: fa_fwd_mfma<D, BF, 1, true><<<grid, block, 0, s>>>(a); break;
+        case 4: fa_fwd_mfma<D, BF, 2, false><<<grid, block, 0, s>>>(a); break;
+        default: fa_fwd_mfma<D, BF, 2, true><<<grid, block, 0, s>>>(a); break;
     }
 }
 
 template <int D, bool BF>
-void launch_pp_d(const fa_kargs& a, bool alibi, bool dense, dim3 grid, hipStream_t s) {
+void launch_pp_d(const fa_kargs& a, int al, bool dense, dim3 grid, hipStream_t s) {
     const dim3 block(PP_THREADS);
-    if (alibi) {
-        if (dense) fa_fwd_pp<D, BF, true, true><<<grid, block, 0, s>>>(a);
-        else fa_fwd_pp<D, BF, true, false><<<grid, block, 0, s>>>(a);
-    } else {
-        if (dense) fa_fwd_pp<D, BF, false, true><<<grid, block, 0, s>>>(a);
-        else fa_fwd_pp<D, BF, false, false><<<grid, block, 0, s>>>(a);
+    switch (al * 2 + (dense ? 1 : 0)) {
+        case 0: fa_fwd_pp<D, BF, 0, false><<<grid, block, 0, s>>>(a); break;
+        case 1: fa_fwd_pp<D, BF, 0, true><<<grid, block, 0, s>>>(a); break;
+        case 2: fa_fwd_pp<D, BF, 1, false><<<grid, block, 0, s>>>(a); break;
+        case 3: fa_fwd_pp<D, BF, 1, true><<<grid, block, 0, s>>>(a); break;
+        case 4: fa_fwd_pp<D, BF, 2, false><<<grid, block, 0, s>>>(a); break;
+        default: fa_fwd_pp<D, BF, 2, true><<<grid, block, 0, s>>>(a); break;
     }
 }
 
 template <typename T>
-void launch_generic_t(const fa_kargs& a, int D, bool alibi, bool dense, dim3 grid, hipStream_t s) {
+void launch_generic_t(const fa_kargs& a, int D, int alibi, bool dense, dim3 grid, hipStream_t s) {
     const dim3 block(GN_BM);
     if (D <= 32) fa_fwd_generic<T, 32><<<grid, block, 0, s>>>(a, dense, alibi);
     else if (D <= 64) fa_fwd_generic<T, 64><<<grid, block, 0, s>>>(a, dense, alibi);
@@ -1123,7 +1163,7 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
                             float* softmax_lse, const fa_dims* dims, int32_t layout,
                             int32_t sparse_mode, int64_t pre_tokens, int64_t next_tokens,
                             const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
-                            const int64_t* prefix, const float* alibi_slopes,
+                            const int64_t* prefix, const float* alibi_slopes, int32_t alibi_mode,
                             const uint8_t* atten_mask, const int64_t* mask_bcast, float scale,
                             void* workspace, size_t workspace_bytes, void* stream) {
     fa_call c;
@@ -1136,6 +1176,7 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     c.actual_seq_kvlen = actual_seq_kvlen;
     c.prefix = prefix;
     c.has_alibi = alibi_slopes != nullptr;
+    c.alibi_mode = alibi_mode;
     c.has_mask = atten_mask != nullptr;
     c.mask_bcast = mask_bcast;
     c.scale = scale;
@@ -1166,9 +1207,10 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     }
     st = upload_tables(p, workspace, s);
     if (st != FA_OK) return st;
-    const fa_kargs a = make_kargs(p, q, k, v, out, softmax_lse, alibi_slopes, atten_mask, workspace, scale);
+    fa_kargs a = make_kargs(p, q, k, v, out, softmax_lse, alibi_slopes, atten_mask, workspace, scale);
+    a.alibi_left = alibi_mode == FA_ALIBI_LEFT ? 1 : 0;
     const dim3 grid(static_cast<unsigned>(nblocks));
-    const bool alibi = alibi_slopes != nullptr;
+    const int alibi = alibi_slopes == nullptr ? 0 : (alibi_mode == FA_ALIBI_SQRT ? 2 : 1);
     const bool dense = sparse_mode == 1;
     (void)hipGetLastError();
     if (p.kernel == FA_KERNEL_PP) {

@@ -58,6 +58,9 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     if (!sizes_only) {
         if (call.check_scale && !(std::isfinite(call.scale) && call.scale > 0.0f))
             return FA_ERR_PARAM_INVALID;
+        if (call.alibi_mode != FA_ALIBI_RIGHT && call.alibi_mode != FA_ALIBI_SQRT &&
+            call.alibi_mode != FA_ALIBI_LEFT)
+            return FA_ERR_PARAM_INVALID;
         if (call.has_alibi && d.D > 128) return FA_ERR_PARAM_INVALID;
         if (call.has_alibi && (mode == 7 || mode == 8)) return FA_ERR_PARAM_INVALID;
         if (mode == 1 && !call.has_mask) return FA_ERR_NULLPTR;

@@ -22,6 +22,7 @@ struct fa_call {
     const int64_t* actual_seq_kvlen = nullptr;
     const int64_t* prefix = nullptr;
     bool has_alibi = false;
+    int32_t alibi_mode = FA_ALIBI_RIGHT;
     bool has_mask = false;
     const int64_t* mask_bcast = nullptr;
     float scale = 1.0f;

@@ -161,25 +161,38 @@ def test_fwd_rejects_before_device_work(lib):
     buf = (ctypes.c_char * 4096)()
     p = ctypes.cast(buf, ctypes.c_void_p)
     d = bnsd()
-    st = lib.fa_fwd(None, p, p, p, p, ctypes.byref(d), 0, 3, 0, 0, None, None, None, None, None, None,
-                    0.125, None, 0, None)
+    right, sqrt_, left = 0, 1, 2
+    st = lib.fa_fwd(None, p, p, p, p, ctypes.byref(d), 0, 3, 0, 0, None, None, None, None, right, None,
+                    None, 0.125, None, 0, None)
     assert st == NULLPTR
     d2 = tnd([3, 2], [3, 6])
     need = fb.fa_fwd_workspace_size(d2, "TND", 3, [3, 5], [3, 9])
     assert need > 0
     st = lib.fa_fwd(p, p, p, p, p, ctypes.byref(d2), 2, 3, 0, 0, fb._i64([3, 5]), fb._i64([3, 9]), None,
-                    None, None, None, 0.125, p, need - 1, None)
+                    None, right, None, None, 0.125, p, need - 1, None)
     assert st == WORKSPACE
     st = lib.fa_fwd(p, p, p, p, p, ctypes.byref(d2), 2, 3, 0, 0, fb._i64([3, 5]), fb._i64([3, 9]), None,
-                    None, None, None, 0.125, None, 0, None)
+                    None, right, None, None, 0.125, None, 0, None)
     assert st == NULLPTR
-    st = lib.fa_fwd(p, p, p, p, p, ctypes.byref(d), 0, 4, 3, -9, None, None, None, None, None, None,
-                    0.125, None, 0, None)
+    st = lib.fa_fwd(p, p, p, p, p, ctypes.byref(d), 0, 4, 3, -9, None, None, None, None, right, None,
+                    None, 0.125, None, 0, None)
     assert st == INVALID
+    # alibi_mode outside FA_ALIBI_RIGHT / FA_ALIBI_SQRT / FA_ALIBI_LEFT is rejected, with or
+    # without slopes
+    for bad in (-1, 3, 99):
+        for slopes in (None, p):
+            st = lib.fa_fwd(p, p, p, p, p, ctypes.byref(d), 0, 3, 0, 0, None, None, None, slopes, bad,
+                            None, None, 0.125, None, 0, None)
+            assert st == INVALID, (bad, slopes)
+    # alibi (any variant) is not allowed with the split modes 7/8
+    for mode in (right, sqrt_, left):
+        st = lib.fa_fwd(p, p, p, p, p, ctypes.byref(d2), 2, 7, 3, 0, fb._i64([3, 5]), fb._i64([3, 9]), None,
+                        p, mode, None, None, 0.125, p, need, None)
+        assert st == INVALID, mode
     # empty problem: nothing to do, OK without pointers
     d0 = bnsd(B=0)
     st = lib.fa_fwd(None, None, None, None, None, ctypes.byref(d0), 0, 3, 0, 0, None, None, None, None,
-                    None, None, 0.125, None, 0, None)
+                    right, None, None, 0.125, None, 0, None)
     assert st == OK
 
 

@@ -1,7 +1,8 @@
 """GPU parity: libfa.so (through its C ABI) against the fp64 oracle on the same seeded inputs.
 
 Tolerances (against the fp64 oracle):
-  fp32 inputs:       max |dO| <= 1e-5, max |dLSE| <= 1e-5
+  fp32 inputs:       max |dO| <= 1e-5, |dLSE| <= 1e-5 max(1, |LSE_ref|) (an fp32 LSE of
+                     magnitude X carries X 2^-24 of its own rounding)
   fp16 / bf16:       |dO| <= 2e-2 + 1e-2 |O_ref| per element, |dLSE| <= 1e-3
   fully masked rows: O == 0 and LSE == -inf exactly
 Mask / visible-pair counts and tile classes are integer work: compared bit-exactly.
@@ -48,7 +49,8 @@ def check(o, lse, ref_o, ref_lse, dtype, what=""):
     if dtype == torch.float32:
         err = np.abs(o - ref_o)
         assert err.max(initial=0) <= 1e-5, f"{what}: max |dO| {err.max()}"
-        assert np.abs(lse[live] - ref_lse[live]).max(initial=0) <= 1e-5, what
+        lse_err = np.abs(lse[live] - ref_lse[live]) / np.maximum(1.0, np.abs(ref_lse[live]))
+        assert lse_err.max(initial=0) <= 1e-5, f"{what}: max relative |dLSE| {lse_err.max(initial=0)}"
     else:
         bound = 2e-2 + 1e-2 * np.abs(ref_o)
         bad = np.abs(o - ref_o) > bound
@@ -235,6 +237,62 @@ def test_parity_dense_mask(gpu_device, alibi):
             ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout=layout, sparse_mode=1, scale=0.1,
                                               atten_mask=mask, alibi_slopes=slopes)
             check(o, lse, ref_o, ref_lse, DT[dtype], f"mode=1 {dtype} {layout} bcast={bc}")
+            zero_rows_ok(o, lse, layout)
+
+
+ALIBI_VARIANTS = [("bf16", 128, "BNSD"), ("f16", 64, "BSND"), ("f32", 16, "BNSD"), ("bf16", 40, "BSND")]
+ALIBI_CASES = [(0, dict(pre_tokens=40, next_tokens=25)), (3, {}), (4, dict(pre_tokens=60, next_tokens=7)),
+               (5, dict(prefix=[250, 10]))]
+ALIBI_SLOPES = [0.6, 0.25, 0.05]
+
+
+@pytest.mark.parametrize("alibi_mode", ["sqrt", "left"])
+def test_parity_alibi_variants(gpu_device, alibi_mode):
+    """Square-root and left-aligned alibi ("压缩mask", alibi scenario) against the oracle: the
+    MFMA kernel (D 128 and 64) and the generic kernel; masks with keys on both sides of the
+    bottom-right diagonal, a prefix, and varlen TND (per-batch diagonal shift)."""
+    for vi, (dtype, D, layout) in enumerate(ALIBI_VARIANTS):
+        for mode, args in ALIBI_CASES:
+            for (sq, skv) in [(300, 200), (130, 333)]:
+                B, N = 2, 3
+                q, k, v = make_inputs(layout, dtype, B, N, sq, skv, D, seed=7000 + 10 * vi + mode)
+                scale = 1.0 / math.sqrt(D)
+                o, lse = run(q, k, v, layout, mode, scale, gpu_device, slopes=ALIBI_SLOPES,
+                             alibi_mode=alibi_mode, **args)
+                ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout=layout, sparse_mode=mode,
+                                                  scale=scale, alibi_slopes=ALIBI_SLOPES, alibi_mode=alibi_mode,
+                                                  **args)
+                check(o, lse, ref_o, ref_lse, DT[dtype],
+                      f"alibi={alibi_mode} mode={mode} {dtype} D={D} {layout} {sq}x{skv} {args}")
+                zero_rows_ok(o, lse, layout)
+    ql, kl = [200, 1, 129, 257], [150, 300, 64, 257]
+    for dtype, D in [("bf16", 128), ("f32", 32)]:
+        q, k, v = make_inputs("TND", dtype, len(ql), 3, 0, 0, D, seed=7100, qlens=ql, kvlens=kl)
+        cq, ck = synth.cumulative_ends(ql), synth.cumulative_ends(kl)
+        o, lse = run(q, k, v, "TND", 3, 0.125, gpu_device, slopes=ALIBI_SLOPES, alibi_mode=alibi_mode,
+                     actual_seq_qlen=cq, actual_seq_kvlen=ck)
+        ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout="TND", sparse_mode=3, scale=0.125,
+                                          actual_seq_qlen=cq, actual_seq_kvlen=ck, alibi_slopes=ALIBI_SLOPES,
+                                          alibi_mode=alibi_mode)
+        check(o, lse, ref_o, ref_lse, DT[dtype], f"alibi={alibi_mode} TND {dtype}")
+
+
+@pytest.mark.parametrize("alibi_mode", [None, "right", "sqrt", "left"])
+def test_parity_mfma32_kernel(gpu_device, alibi_mode, monkeypatch):
+    """The 4-wave MFMA kernel (FA_KERNEL=mfma32, kept for comparisons) against the oracle."""
+    monkeypatch.setenv("FA_KERNEL", "mfma32")
+    dims = fb.make_dims(torch.bfloat16, 0, B=1, N=1, Sq=8, Skv=8, D=128)
+    assert fb.fa_tile_shape(dims, "BNSD")[:2] == (128, 64)
+    slopes = ALIBI_SLOPES if alibi_mode else None
+    for dtype, D, layout in [("bf16", 128, "BNSD"), ("f16", 64, "BSND")]:
+        for mode, args in [(0, dict(pre_tokens=9, next_tokens=-3))] + ALIBI_CASES[1:]:
+            q, k, v = make_inputs(layout, dtype, 2, 3, 300, 333, D, seed=7200 + mode)
+            kw = dict(alibi_mode=alibi_mode) if alibi_mode else {}
+            o, lse = run(q, k, v, layout, mode, 0.1, gpu_device, slopes=slopes, **kw, **args)
+            ref_o, ref_lse = oracle.attention(to64(q), to64(k), to64(v), layout=layout, sparse_mode=mode,
+                                              scale=0.1, alibi_slopes=slopes, alibi_mode=alibi_mode or "right",
+                                              **args)
+            check(o, lse, ref_o, ref_lse, DT[dtype], f"mfma32 alibi={alibi_mode} mode={mode} {dtype} {layout}")
             zero_rows_ok(o, lse, layout)
 
 
