@@ -124,6 +124,45 @@ def cpu_baseline(w, heads: int):
                       f"{t_total:.1f} s of fp64 numpy (BLAS threads={threads}, elementwise on 1 core)"}
 
 
+def bench_scatter(args, dev):
+    """Paged KV cache scatter ("aclnnScatterPaKvCache", Norm cache): a prefill chunk of
+    32768 tokens x 32 heads x D 128 bf16 keys and values written to random distinct slots of a
+    65536-slot cache (512 blocks of 128). HBM-bound: every byte is read once and written once."""
+    import torch
+    from masked_attention_forward_amd import binding as fb
+
+    T, N, D, nb, bs = 32768, 32, 128, 512, 128
+    g = torch.Generator().manual_seed(11)
+    key = torch.randn(T, N, D, generator=g).to(torch.bfloat16).to(dev)
+    val = torch.randn(T, N, D, generator=g).to(torch.bfloat16).to(dev)
+    kc = torch.zeros(nb, bs, N, D, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    slots = torch.randperm(nb * bs, generator=g)[:T].to(torch.int64).to(dev)
+    for _ in range(args.warmup):
+        fb.fa_scatter_kv_cache(key, kc, slots, val, vc)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fb.fa_scatter_kv_cache(key, kc, slots, val, vc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    moved = 2 * 2 * T * N * D * 2 + T * 8   # K and V read + written, plus the slots
+    gbs = moved / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "paged KV cache scatter bandwidth (bytes read + written)", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) keys/values, random distinct slots)",
+        "config": {"workload": "kv_scatter_prefill", "num_tokens": T, "N": N, "D": D, "num_blocks": nb,
+                   "block_size": bs, "layout": "Norm"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "algorithmic_bytes": moved}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +174,8 @@ def main():
                     help="alibi variant for workloads with alibi")
     ap.add_argument("--cpu-heads", type=int, default=48,
                     help="(batch, head) slices of the workload the CPU oracle is timed on")
+    ap.add_argument("--op", default="attention", choices=["attention", "scatter_kv"],
+                    help="attention (the default metric) or the paged KV cache scatter")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(reference for the HBM byte counters)")
@@ -157,6 +198,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": args.warmup + args.steps}))
+        return
+    if args.op == "scatter_kv":
+        bench_scatter(args, dev)
         return
     w = synth.workloads()[args.workload]
     q, k, v = (x.to(dev) for x in w.tensors())

@@ -175,6 +175,43 @@ fa_status fa_plan_stats_get(const fa_dims* dims, int32_t layout, int32_t sparse_
 /* A static, human-readable name for a status code. */
 const char* fa_status_str(fa_status status);
 
+/* ---------------------------------------------------------------------------------------
+ * Paged KV cache ("aclnnScatterPaKvCache", sections "功能说明" and "约束说明").
+ * --------------------------------------------------------------------------------------- */
+
+/* Cache layouts. A slot is block * block_size + offset.
+ *   FA_CACHE_NORM: [num_blocks, block_size, N, head_size] (the page's scenario two, "Norm");
+ *   FA_CACHE_NHSD: [num_blocks, N, block_size, head_size] (scenario seven, "NHSD"). */
+#define FA_CACHE_NORM 0
+#define FA_CACHE_NHSD 1
+
+typedef struct fa_kv_cache_dims {
+    int64_t num_tokens;   /* tokens to write (key is [num_tokens, N, k_head_size])       */
+    int64_t num_heads;    /* N                                                           */
+    int64_t k_head_size;
+    int64_t v_head_size;  /* ignored when value is NULL (keys only, scenario six)        */
+    int64_t num_blocks;
+    int64_t block_size;
+    int32_t elem_bytes;   /* bytes per element of key / value / caches: 1, 2 or 4 (raw copy) */
+    int32_t slot_bytes;   /* slot_mapping element: 4 (int32) or 8 (int64)                */
+} fa_kv_cache_dims;
+
+/* Scatter: for every token t and head h, key[t, h, :] goes to key_cache at slot
+ * slot_mapping[t] (and value[t, h, :] to value_cache).
+ *   key, value:             device, contiguous [num_tokens, N, head_size]; value may be NULL
+ *                           (then value_cache must be NULL too).
+ *   key_cache, value_cache: device, contiguous in cache_layout; updated in place.
+ *   slot_mapping:           device int32 or int64 [num_tokens]. Slots must be distinct; a
+ *                           slot outside [0, num_blocks * block_size - 1] (for example -1
+ *                           for a padding token) writes nothing.
+ * Errors: NULLPTR for a missing required pointer (when num_tokens > 0, or dims itself);
+ * PARAM_INVALID for an unknown layout or element size or non-positive sizes; UNSUPPORTED for
+ * sizes beyond 32-bit row offsets; HIP for a launch error. Asynchronous on `stream`; no
+ * workspace, no allocation; deterministic. */
+fa_status fa_scatter_kv_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                              const void* slot_mapping, const fa_kv_cache_dims* dims,
+                              int32_t cache_layout, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

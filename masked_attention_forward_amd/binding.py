@@ -40,6 +40,15 @@ class FaError(RuntimeError):
         super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({fa_status_str(status)})")
 
 
+class FaKvCacheDims(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int64), ("num_heads", ctypes.c_int64),
+                ("k_head_size", ctypes.c_int64), ("v_head_size", ctypes.c_int64),
+                ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int64),
+                ("elem_bytes", ctypes.c_int32), ("slot_bytes", ctypes.c_int32)]
+
+
+CACHE_LAYOUTS = {"Norm": 0, "NHSD": 1}
+
 _LIB = None
 
 
@@ -75,6 +84,8 @@ def load_library():
     lib.fa_plan_stats_get.restype = i32
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_scatter_kv_cache.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(FaKvCacheDims), i32, vp]
+    lib.fa_scatter_kv_cache.restype = i32
     _LIB = lib
     return lib
 
@@ -184,6 +195,45 @@ def _alibi_code(mode) -> int:
             raise ValueError(f"alibi_mode must be one of {sorted(ALIBI_MODES)}")
         return ALIBI_MODES[mode]
     return int(mode)
+
+
+def fa_scatter_kv_cache(key, key_cache, slot_mapping, value=None, value_cache=None, *, layout="Norm",
+                        stream=None) -> None:
+    """Writes key[t] (and value[t]) into the cache slot slot_mapping[t] (in place).
+
+    key / value: [num_tokens, N, D]; caches: [num_blocks, block_size, N, D] ("Norm") or
+    [num_blocks, N, block_size, D] ("NHSD"); slot_mapping int32 or int64 [num_tokens]."""
+    lib = load_library()
+    if layout not in CACHE_LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(CACHE_LAYOUTS)}")
+    if (value is None) != (value_cache is None):
+        raise ValueError("value and value_cache go together")
+    for name, t in (("key", key), ("key_cache", key_cache), ("value", value), ("value_cache", value_cache)):
+        _check_device_tensor(name, t, key.dtype)
+    _check_device_tensor("slot_mapping", slot_mapping)
+    if slot_mapping.dtype not in (torch.int32, torch.int64) or slot_mapping.dim() != 1:
+        raise TypeError("slot_mapping must be a 1-D int32 or int64 tensor")
+    if key.dim() != 3 or key_cache.dim() != 4:
+        raise ValueError("key must be [num_tokens, N, D] and key_cache 4-D")
+    t, n, dk = key.shape
+    nb = key_cache.shape[0]
+    bs = key_cache.shape[1] if layout == "Norm" else key_cache.shape[2]
+    want = (nb, bs, n, dk) if layout == "Norm" else (nb, n, bs, dk)
+    if tuple(key_cache.shape) != want or slot_mapping.shape[0] != t:
+        raise ValueError(f"shapes: key {tuple(key.shape)}, key_cache {tuple(key_cache.shape)}, "
+                         f"slot_mapping {tuple(slot_mapping.shape)}")
+    dv = 0
+    if value is not None:
+        dv = value.shape[-1]
+        want_v = (nb, bs, n, dv) if layout == "Norm" else (nb, n, bs, dv)
+        if tuple(value.shape) != (t, n, dv) or tuple(value_cache.shape) != want_v:
+            raise ValueError(f"shapes: value {tuple(value.shape)}, value_cache {tuple(value_cache.shape)}")
+    dims = FaKvCacheDims(t, n, dk, dv, nb, bs, key.element_size(), slot_mapping.element_size())
+    st = lib.fa_scatter_kv_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                 _ptr(slot_mapping), ctypes.byref(dims), CACHE_LAYOUTS[layout],
+                                 stream if stream is not None else _stream(key.device))
+    if st != 0:
+        raise FaError(st, "fa_scatter_kv_cache")
 
 
 def lse_shape(q, layout, actual_seq_qlen=None):

@@ -300,3 +300,37 @@ def test_plan_tiles_varlen_match_brute_force(lib, mode):
             vt += v
             ft += f
         assert (st["kv_tiles_visited"], st["kv_tiles_full"]) == (vt, ft), (ql, kl, pre, nxt)
+
+
+# ---------------------------------------------------------------------------------------
+# Paged KV cache scatter: host validation (no device work)
+# ---------------------------------------------------------------------------------------
+
+def test_scatter_kv_cache_validation(lib):
+    """fa_scatter_kv_cache checks its arguments before any launch ("aclnnScatterPaKvCache",
+    return-code table): missing pointers, unknown layout / element size / slot type, and
+    non-positive sizes; an empty token list is a no-op."""
+    buf = (ctypes.c_char * 4096)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+
+    def dims(**kw):
+        base = dict(num_tokens=4, num_heads=2, k_head_size=8, v_head_size=8, num_blocks=3, block_size=2,
+                    elem_bytes=2, slot_bytes=4)
+        base.update(kw)
+        return fb.FaKvCacheDims(**base)
+
+    call = lambda d, key=p, val=p, kc=p, vc=p, slots=p, layout=0: lib.fa_scatter_kv_cache(
+        key, val, kc, vc, slots, ctypes.byref(d) if d is not None else None, layout, None)
+    assert call(None) == NULLPTR
+    assert call(dims(), key=None) == NULLPTR
+    assert call(dims(), kc=None) == NULLPTR
+    assert call(dims(), slots=None) == NULLPTR
+    assert call(dims(), val=None) == NULLPTR            # value_cache without value
+    assert call(dims(), layout=2) == INVALID
+    assert call(dims(elem_bytes=3)) == INVALID
+    assert call(dims(slot_bytes=2)) == INVALID
+    assert call(dims(num_heads=0)) == INVALID
+    assert call(dims(block_size=0)) == INVALID
+    assert call(dims(num_tokens=-1)) == INVALID
+    assert call(dims(num_tokens=0), key=None, val=None, kc=None, vc=None, slots=None) == OK
+    assert call(dims(num_heads=1 << 17)) == UNSUPPORTED
