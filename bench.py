@@ -2,9 +2,10 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step is one fa_fwd call over the whole workload (inputs already resident in HBM). The
-metric is effective TFLOP/s: 4 * D flops per visible (query, key) pair, summed over batches
-and heads, divided by the step time; masked or skipped work is never counted. The visible
+One step is one fa_fwd call (fa_fwd_paged with --block-size) over the whole workload (inputs
+already resident in HBM). The metric is effective TFLOP/s: 4 * D flops per visible (query,
+key) pair, summed over batches and heads, divided by the step time; masked or skipped work
+is never counted. The visible
 pair count comes from the library's mask probe (checked bit-exactly against the oracle by
 the test suite) and is cross-checked against a closed form where one exists.
 
@@ -124,6 +125,45 @@ def cpu_baseline(w, heads: int):
                       f"{t_total:.1f} s of fp64 numpy (BLAS threads={threads}, elementwise on 1 core)"}
 
 
+def paged_caches(w, k, v, bs, cache_layout, dev):
+    """K / V of workload w moved into paged caches ("aclnnScatterPaKvCache" layouts) with
+    randomly permuted distinct pages; returns (key_cache, value_cache, block_table int32)."""
+    import numpy as np
+    import torch
+
+    if w.layout == "BNSD":
+        seqs_k = [k[b].transpose(0, 1) for b in range(w.B)]
+        seqs_v = [v[b].transpose(0, 1) for b in range(w.B)]
+    elif w.layout == "BSND":
+        seqs_k, seqs_v = [k[b] for b in range(w.B)], [v[b] for b in range(w.B)]
+    else:
+        ends = w.actual_seq_kvlen
+        starts = [0] + list(ends[:-1])
+        seqs_k = [k[s:e] for s, e in zip(starts, ends)]
+        seqs_v = [v[s:e] for s, e in zip(starts, ends)]
+    lens = [int(x.shape[0]) for x in seqs_k]
+    need = [-(-L // bs) for L in lens]
+    nb = sum(need)
+    perm = np.random.default_rng(17).permutation(nb)
+    bt = np.zeros((len(lens), max(need + [1])), dtype=np.int32)
+    p = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[p:p + n]
+        p += n
+    N, D = w.N, w.D
+    shape = (nb, bs, N, D) if cache_layout == "Norm" else (nb, N, bs, D)
+    caches = []
+    for seqs in (seqs_k, seqs_v):
+        c = torch.zeros(shape, dtype=k.dtype, device=dev)
+        view = c if cache_layout == "Norm" else c.permute(0, 2, 1, 3)
+        for b, s in enumerate(seqs):
+            j = torch.arange(lens[b], device=dev)
+            pages = torch.from_numpy(bt[b].astype(np.int64)).to(dev)[j // bs]
+            view[pages, j % bs] = s
+        caches.append(c)
+    return caches[0], caches[1], torch.from_numpy(bt).to(dev)
+
+
 def bench_scatter(args, dev):
     """Paged KV cache scatter ("aclnnScatterPaKvCache", Norm cache): a prefill chunk of
     32768 tokens x 32 heads x D 128 bf16 keys and values written to random distinct slots of a
@@ -176,6 +216,10 @@ def main():
                     help="(batch, head) slices of the workload the CPU oracle is timed on")
     ap.add_argument("--op", default="attention", choices=["attention", "scatter_kv"],
                     help="attention (the default metric) or the paged KV cache scatter")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="> 0: read K / V through fa_fwd_paged from caches of pages of this many keys")
+    ap.add_argument("--cache-layout", default="Norm", choices=["Norm", "NHSD"],
+                    help="paged cache layout (with --block-size)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(reference for the HBM byte counters)")
@@ -208,12 +252,28 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty(fb.lse_shape(q, w.layout), dtype=torch.float32, device=dev)
     dims = fb.dims_of(q, k, w.layout, w.actual_seq_qlen)
-    ws_bytes = fb.fa_fwd_workspace_size(dims, w.layout, w.sparse_mode, w.actual_seq_qlen, w.actual_seq_kvlen)
+    paged = None
+    if args.block_size > 0:
+        paged = paged_caches(w, k, v, args.block_size, args.cache_layout, dev)
+        pk = fb.paged_kv(paged[2], paged[0], cache_layout=args.cache_layout)
+        ws_bytes = fb.fa_fwd_paged_workspace_size(dims, w.layout, w.sparse_mode, pk, w.actual_seq_qlen,
+                                                  w.actual_seq_kvlen)
+    else:
+        ws_bytes = fb.fa_fwd_workspace_size(dims, w.layout, w.sparse_mode, w.actual_seq_qlen, w.actual_seq_kvlen)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     kw = dict(layout=w.layout, sparse_mode=w.sparse_mode, pre_tokens=w.pre_tokens, next_tokens=w.next_tokens,
               actual_seq_qlen=w.actual_seq_qlen, actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix,
               alibi_slopes=slopes, alibi_mode=args.alibi_mode, scale=w.softmax_scale,
               workspace=ws if ws_bytes else None)
+    if paged is not None:
+        kc, vc, bt = paged
+        pkw = dict(kw, cache_layout=args.cache_layout, kv_seqlen=w.Skv)
+
+        def step():
+            fb.fa_fwd_paged(q, kc, vc, bt, out, lse, **pkw)
+    else:
+        def step():
+            fb.fa_fwd(q, k, v, out, lse, **kw)
     pairs = visible_pairs(w, dev)
     flops = 4 * w.D * pairs
     elem = q.element_size()
@@ -222,19 +282,19 @@ def main():
     alg_bytes = (2 * rows_q * w.D + 2 * rows_kv * w.D) * elem + 4 * rows_q
 
     for _ in range(args.warmup):
-        fb.fa_fwd(q, k, v, out, lse, **kw)
+        step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        fb.fa_fwd(q, k, v, out, lse, **kw)
+        step()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = recorded_traffic(args.workload)
+    traffic = recorded_traffic(args.workload) if paged is None else None
 
     res = {
         "metric": METRIC,
@@ -253,7 +313,9 @@ def main():
                    "B": w.B, "N": w.N, "Sq": w.Sq, "Skv": w.Skv, "D": w.D,
                    "pre_tokens": w.pre_tokens, "next_tokens": w.next_tokens,
                    "alibi": (args.alibi_mode if w.alibi else False), "visible_pairs": pairs,
-                   "flop_per_step": flops},
+                   "flop_per_step": flops,
+                   "paged_kv": ({"block_size": args.block_size, "cache_layout": args.cache_layout}
+                                if paged is not None else None)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,

@@ -212,6 +212,54 @@ fa_status fa_scatter_kv_cache(const void* key, const void* value, void* key_cach
                               const void* slot_mapping, const fa_kv_cache_dims* dims,
                               int32_t cache_layout, void* stream);
 
+/* Where a sequence's keys live in a paged cache. Sequence b's key j (j counted from the
+ * sequence's first key) is in page block_table[b * max_blocks_per_seq + j / block_size] at
+ * offset j % block_size, i.e. in the slot that fa_scatter_kv_cache writes for
+ * slot = page * block_size + j % block_size. The pages describe the cache and its slots; this
+ * read-back rule is the plain reading of "slot = block * block_size + offset".
+ *   block_table:        device int32 [B, max_blocks_per_seq]; entries past a sequence's last
+ *                       page are not read. Every page a sequence uses must lie in
+ *                       [0, num_blocks): an id outside it reads as zeros (no access outside
+ *                       the cache), which gives a defined but meaningless result.
+ *   max_blocks_per_seq: row length of block_table; max_blocks_per_seq * block_size must cover
+ *                       the longest sequence.
+ *   num_blocks, block_size, cache_layout: as for fa_scatter_kv_cache (FA_CACHE_NORM or
+ *                       FA_CACHE_NHSD); head_size of the caches is dims->D. */
+typedef struct fa_paged_kv {
+    const int32_t* block_table;
+    int64_t max_blocks_per_seq;
+    int64_t num_blocks;
+    int64_t block_size;
+    int32_t cache_layout;
+    int32_t reserved;      /* must be 0 */
+} fa_paged_kv;
+
+/* Workspace size of fa_fwd_paged for these sizes (host only, like fa_fwd_workspace_size; it
+ * can differ from fa_fwd's because the kernel choice depends on the page size). */
+fa_status fa_fwd_paged_workspace_size(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                                      const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                                      const fa_paged_kv* paged, size_t* bytes);
+
+/* fa_fwd with K and V read from paged caches instead of contiguous tensors.
+ *   q, out, softmax_lse: as for fa_fwd, in `layout`.
+ *   key_cache, value_cache: device, dims->dtype, [num_blocks, block_size, N, D] (Norm) or
+ *                        [num_blocks, N, block_size, D] (NHSD).
+ *   dims:                as for fa_fwd; Skv (BNSD / BSND) or actual_seq_kvlen (TND) give the
+ *                        key count of each sequence, T_kv must equal the last kvlen entry.
+ *   workspace:           at least fa_fwd_paged_workspace_size bytes.
+ * Every other argument, the status codes and the results are fa_fwd's: the output equals
+ * fa_fwd's on the gathered K and V (bitwise when both calls run the same kernel). PARAM_INVALID for a bad fa_paged_kv (unknown layout, non-positive sizes,
+ * reserved != 0, or a table too short for the longest sequence); NULLPTR when paged or a
+ * cache or block_table is missing while some sequence has keys. */
+fa_status fa_fwd_paged(const void* q, const void* key_cache, const void* value_cache, void* out,
+                       float* softmax_lse, const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                       int64_t pre_tokens, int64_t next_tokens,
+                       const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                       const int64_t* prefix, const float* alibi_slopes, int32_t alibi_mode,
+                       const uint8_t* atten_mask, const int64_t* mask_bcast,
+                       const fa_paged_kv* paged, float scale, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,12 @@ class FaKvCacheDims(ctypes.Structure):
 
 CACHE_LAYOUTS = {"Norm": 0, "NHSD": 1}
 
+
+class FaPagedKv(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int64),
+                ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int64),
+                ("cache_layout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
 _LIB = None
 
 
@@ -86,6 +92,12 @@ def load_library():
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_scatter_kv_cache.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(FaKvCacheDims), i32, vp]
     lib.fa_scatter_kv_cache.restype = i32
+    ppaged = ctypes.POINTER(FaPagedKv)
+    lib.fa_fwd_paged_workspace_size.argtypes = [pdims, i32, i32, pi64, pi64, ppaged, ctypes.POINTER(sz)]
+    lib.fa_fwd_paged_workspace_size.restype = i32
+    lib.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
+                                 vp, i32, vp, pi64, ppaged, ctypes.c_float, vp, sz, vp]
+    lib.fa_fwd_paged.restype = i32
     _LIB = lib
     return lib
 
@@ -234,6 +246,108 @@ def fa_scatter_kv_cache(key, key_cache, slot_mapping, value=None, value_cache=No
                                  stream if stream is not None else _stream(key.device))
     if st != 0:
         raise FaError(st, "fa_scatter_kv_cache")
+
+
+def paged_kv(block_table: Optional[torch.Tensor], key_cache: torch.Tensor, *, cache_layout="Norm",
+             max_blocks_per_seq: Optional[int] = None) -> FaPagedKv:
+    """fa_paged_kv for a cache tensor ([num_blocks, block_size, N, D] for "Norm",
+    [num_blocks, N, block_size, D] for "NHSD") and an int32 block table [B, max_blocks_per_seq]."""
+    if cache_layout not in CACHE_LAYOUTS:
+        raise ValueError(f"cache_layout must be one of {sorted(CACHE_LAYOUTS)}")
+    if key_cache.dim() != 4:
+        raise ValueError("key_cache must be 4-D")
+    nb = key_cache.shape[0]
+    bs = key_cache.shape[1] if cache_layout == "Norm" else key_cache.shape[2]
+    if max_blocks_per_seq is None:
+        max_blocks_per_seq = block_table.shape[1] if block_table is not None and block_table.dim() == 2 else 1
+    return FaPagedKv(block_table.data_ptr() if block_table is not None and block_table.numel() else None,
+                     int(max_blocks_per_seq), int(nb), int(bs), CACHE_LAYOUTS[cache_layout], 0)
+
+
+def paged_dims(q: torch.Tensor, layout, *, kv_seqlen: int = 0, actual_seq_qlen=None,
+               actual_seq_kvlen=None) -> FaDims:
+    """fa_dims of a paged call: q's shape, and Skv = kv_seqlen (BNSD / BSND) or
+    T_kv = actual_seq_kvlen[-1] (TND)."""
+    lay = _layout_code(layout)
+    if q.dtype not in _DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if lay == 0:
+        B, N, Sq, D = q.shape
+        return make_dims(q.dtype, lay, B=B, N=N, Sq=Sq, Skv=int(kv_seqlen), D=D)
+    if lay == 1:
+        B, Sq, N, D = q.shape
+        return make_dims(q.dtype, lay, B=B, N=N, Sq=Sq, Skv=int(kv_seqlen), D=D)
+    T_q, N, D = q.shape
+    B = len(actual_seq_qlen) if actual_seq_qlen is not None else 0
+    T_kv = int(actual_seq_kvlen[-1]) if actual_seq_kvlen is not None and len(actual_seq_kvlen) else 0
+    return make_dims(q.dtype, lay, B=B, N=N, D=D, T_q=T_q, T_kv=T_kv)
+
+
+def fa_fwd_paged_workspace_size(dims: FaDims, layout, sparse_mode: int, paged: FaPagedKv,
+                                actual_seq_qlen=None, actual_seq_kvlen=None) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    st = lib.fa_fwd_paged_workspace_size(ctypes.byref(dims), _layout_code(layout), int(sparse_mode),
+                                         _i64(actual_seq_qlen), _i64(actual_seq_kvlen), ctypes.byref(paged),
+                                         ctypes.byref(out))
+    if st != 0:
+        raise FaError(st, "fa_fwd_paged_workspace_size")
+    return int(out.value)
+
+
+def fa_fwd_paged(q, key_cache, value_cache, block_table, out, softmax_lse, *, layout="BNSD",
+                 cache_layout="Norm", kv_seqlen: int = 0, sparse_mode: int = 0, pre_tokens: int = 0,
+                 next_tokens: int = 0, actual_seq_qlen=None, actual_seq_kvlen=None, prefix=None,
+                 alibi_slopes: Optional[torch.Tensor] = None, alibi_mode="right",
+                 atten_mask: Optional[torch.Tensor] = None, mask_bcast=None, scale: float,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Calls fa_fwd_paged: K / V from paged caches through an int32 block table
+    [B, max_blocks_per_seq]. kv_seqlen is Skv for BNSD / BSND (TND uses actual_seq_kvlen)."""
+    lib = load_library()
+    for name, t in (("q", q), ("key_cache", key_cache), ("value_cache", value_cache), ("out", out)):
+        _check_device_tensor(name, t, q.dtype)
+    _check_device_tensor("softmax_lse", softmax_lse, torch.float32)
+    _check_device_tensor("block_table", block_table, torch.int32)
+    _check_device_tensor("alibi_slopes", alibi_slopes, torch.float32)
+    if atten_mask is not None:
+        _check_device_tensor("atten_mask", atten_mask)
+        if atten_mask.dtype not in (torch.uint8, torch.bool):
+            raise TypeError("atten_mask must be uint8 or bool")
+    if key_cache.shape != value_cache.shape:
+        raise ValueError("key_cache and value_cache must have one shape")
+    head = key_cache.shape[2] if cache_layout == "Norm" else key_cache.shape[1]
+    if key_cache.shape[3] != q.shape[-1] or head != (q.shape[1] if _layout_code(layout) != 1 else q.shape[2]):
+        raise ValueError(f"cache {tuple(key_cache.shape)} does not match q {tuple(q.shape)} ({layout}, {cache_layout})")
+    dims = paged_dims(q, layout, kv_seqlen=kv_seqlen, actual_seq_qlen=actual_seq_qlen,
+                      actual_seq_kvlen=actual_seq_kvlen)
+    if block_table is not None and block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    pk = paged_kv(block_table, key_cache, cache_layout=cache_layout)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.fa_fwd_paged(_ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(out), _ptr(softmax_lse),
+                          ctypes.byref(dims), _layout_code(layout), int(sparse_mode), int(pre_tokens),
+                          int(next_tokens), _i64(actual_seq_qlen), _i64(actual_seq_kvlen), _i64(prefix),
+                          _ptr(alibi_slopes), _alibi_code(alibi_mode), _ptr(atten_mask), _i64(mask_bcast),
+                          ctypes.byref(pk), float(scale), _ptr(workspace), ws_bytes,
+                          stream if stream is not None else _stream(q.device))
+    if st != 0:
+        raise FaError(st, "fa_fwd_paged")
+
+
+def paged_attention(q, key_cache, value_cache, block_table, *, layout="BNSD", cache_layout="Norm",
+                    kv_seqlen: int = 0, sparse_mode: int = 0, scale: float, **kw):
+    """Allocates out / softmax_lse / workspace and runs fa_fwd_paged. Returns (out, softmax_lse)."""
+    out = torch.empty_like(q)
+    lse = torch.empty(lse_shape(q, layout), dtype=torch.float32, device=q.device)
+    dims = paged_dims(q, layout, kv_seqlen=kv_seqlen, actual_seq_qlen=kw.get("actual_seq_qlen"),
+                      actual_seq_kvlen=kw.get("actual_seq_kvlen"))
+    pk = paged_kv(block_table, key_cache, cache_layout=cache_layout)
+    ws = fa_fwd_paged_workspace_size(dims, layout, sparse_mode, pk, kw.get("actual_seq_qlen"),
+                                     kw.get("actual_seq_kvlen"))
+    workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    fa_fwd_paged(q, key_cache, value_cache, block_table, out, lse, layout=layout, cache_layout=cache_layout,
+                 kv_seqlen=kv_seqlen, sparse_mode=sparse_mode, scale=scale, workspace=workspace, **kw)
+    return out, lse
 
 
 def lse_shape(q, layout, actual_seq_qlen=None):

@@ -1,5 +1,5 @@
 // fa_kernels.hip - masked attention forward kernels for gfx950 (MI355X) and the device half
-// of the C ABI (fa_fwd, fa_mask_probe).
+// of the C ABI (fa_fwd, fa_fwd_paged, fa_mask_probe).
 //
 // The method is FlashAttention-style tiling with an online softmax ("Ý Tưởng Tiling & Online
 // Softmax Trong FlashAttention", knowledge goals): K/V blocks stream past a block of query
@@ -25,6 +25,12 @@
 //    throughout (P is never rounded), K/V tiles of 16 keys staged in LDS.
 // All visit only kv tiles that hold a visible entry (fa_tile_kv_range) and skip per-element
 // masking on tiles that are fully visible (fa_tile_full).
+//
+// Paged K / V (fa_fwd_paged): K and V come from the caches that fa_scatter_kv_cache fills
+// ("aclnnScatterPaKvCache", layouts "Norm" and "NHSD"), key j of sequence b in page
+// block_table[b][j / block_size]. The ping-pong kernel takes it when pages hold a power of two
+// >= 64 keys (one page per 64-key tile: only the tile's base address changes); the generic
+// kernel takes every other page size and explicit masks.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -62,6 +68,13 @@ struct fa_kargs {
     int32_t xcd_major;      // fixed-length launch order, see fa_decode_item
     int32_t alibi_left;     // linear alibi measured from the top-left diagonal (else bottom-right)
     float scale_log2;       // scale * log2(e)
+    // Paged K / V (k and v are the caches; kv_bs = 0, sequences start at key 0 of their pages).
+    const int32_t* block_table;   // [B, bt_stride] page ids, or nullptr
+    int64_t page_stride;          // elements from one page to the next
+    int64_t bt_stride;
+    int32_t block_size;
+    int32_t log2_block_size;      // ping-pong kernel: block_size = 2^log2_block_size >= 64
+    int32_t num_pages;            // valid page ids are [0, num_pages)
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -579,7 +592,7 @@ __device__ __forceinline__ void fa_lds_barrier_pending() {
 // s_waitcnt immediate for vmcnt(n) alone (n < 16).
 constexpr int fa_vmcnt(int n) { return 0x0F70 | n; }
 
-template <int D, bool IS_BF16, int AL, bool DENSE>
+template <int D, bool IS_BF16, int AL, bool DENSE, bool PAGED = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(PP_THREADS, PP_THREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 fa_fwd_pp(const fa_kargs a) {
@@ -598,6 +611,8 @@ fa_fwd_pp(const fa_kargs a) {
 
     __shared__ u32x4 lds_k0[TILE_CHUNKS], lds_k1[TILE_CHUNKS], lds_k2[TILE_CHUNKS], lds_k3[TILE_CHUNKS];
     __shared__ u32x4 lds_v0[TILE_CHUNKS], lds_v1[TILE_CHUNKS], lds_v2[TILE_CHUNKS], lds_v3[TILE_CHUNKS];
+    // Paged K / V: ids of the pages this item's key range touches, first page first.
+    __shared__ int32_t lds_pages[PAGED ? FA_PP_MAX_PAGES : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -648,6 +663,36 @@ fa_fwd_pp(const fa_kargs a) {
     const uint8_t* mrow = nullptr;
     if (DENSE) mrow = a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs;
 
+    // Paged K / V: a 64-key tile lies inside one page (pages hold 2^lbs >= 64 keys). The ids of
+    // pages pg_first .. (kv_lim - 1) >> lbs go to LDS once; a tile's id is read from there one
+    // phase before its load, so no scalar memory load (and its full lgkmcnt wait) sits in the
+    // loop.
+    int lbs = 0, pg_first = 0, n_pages = 0;
+    int64_t pg_stride = 0;
+    if constexpr (PAGED) {
+        lbs = a.log2_block_size;
+        n_pages = a.num_pages;
+        pg_stride = a.page_stride;
+        asm volatile("" : : "s"(lbs), "s"(n_pages), "s"(pg_stride));
+        if (n_tiles > 0) {
+            pg_first = (kr.begin * BN) >> lbs;
+            const int cnt = ((kv_lim - 1) >> lbs) - pg_first + 1;
+            const int32_t* bt = a.block_table + b * a.bt_stride + pg_first;
+            for (int e = tid; e < cnt; e += NT) lds_pages[e] = bt[e];
+        }
+        __syncthreads();
+    }
+    // Page id of key tile kt (-1 past the item's range: that load reads nothing).
+    auto page_of = [&](int kt) __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+            const int e = min(max(((kt * BN) >> lbs) - pg_first, 0), FA_PP_MAX_PAGES - 1);
+            const int pg = fa_uniform(lds_pages[e]);
+            return kt < kr.end ? pg : -1;
+        } else {
+            return 0;
+        }
+    };
+
     float m_run = -INFINITY;
     float l_run = 0.f;
     f32x16 oacc[DBLK];
@@ -662,11 +707,17 @@ fa_fwd_pp(const fa_kargs a) {
         return (j * kv_rs + fa_swz<KCH>(j, P % KCH) * 8) * 2;
     };
     const int dl0 = dl_offset(0), dl1 = LOADS > 1 ? dl_offset(1) : 0;
-    auto dload = [&](const uint16_t* base, int kt, u32x4* dst) __attribute__((always_inline)) {
+    // Tile kt of K or V; `page` is its page id (paged K / V only). Rows past kv_lim, and every
+    // row of a page id outside [0, num_pages), read as zeros.
+    auto dload = [&](const uint16_t* base, int kt, int page, u32x4* dst) __attribute__((always_inline)) {
         const int j0 = kt * BN;
-        const int rows = min(BN, kv_lim - j0);
-        const __amdgpu_buffer_rsrc_t r =
-            fa_rsrc(base + int64_t(j0) * kv_rs, rows > 0 ? ((rows - 1) * kv_rs + D) * 2 : 0);
+        int rows = min(BN, kv_lim - j0);
+        const uint16_t* tile = base + int64_t(j0) * kv_rs;
+        if constexpr (PAGED) {
+            rows = unsigned(page) < unsigned(n_pages) ? rows : 0;
+            tile = base + int64_t(page) * pg_stride + int64_t(j0 & ((1 << lbs) - 1)) * kv_rs;
+        }
+        const __amdgpu_buffer_rsrc_t r = fa_rsrc(tile, rows > 0 ? ((rows - 1) * kv_rs + D) * 2 : 0);
 #pragma unroll
         for (int p = 0; p < LOADS; ++p)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + (wave_u * LOADS + p) * 64), 16,
@@ -851,13 +902,14 @@ fa_fwd_pp(const fa_kargs a) {
         const u32x4* v_cur = S == 0 ? lds_v0 : (S == 1 ? lds_v1 : (S == 2 ? lds_v2 : lds_v3));
         u32x4* k_fill = F == 0 ? lds_k0 : (F == 1 ? lds_k1 : (F == 2 ? lds_k2 : lds_k3));
         u32x4* v_fill = F == 0 ? lds_v0 : (F == 1 ? lds_v1 : (F == 2 ? lds_v2 : lds_v3));
+        const int pg_v = page_of(kr.begin + t + 3), pg_k = page_of(kr.begin + t + 4);
         softmax(t);
         prefetch(v_cur);
         fa_lds_barrier_pending<2 * NPRE>();   // the prefetched V^T reads may still be in flight
         __builtin_amdgcn_s_setprio(1);
         matmul(k_cur, v_cur, [&]() __attribute__((always_inline)) {
-            dload(vp, kr.begin + t + 3, v_fill);
-            dload(kp, kr.begin + t + 4, k_fill);
+            dload(vp, kr.begin + t + 3, pg_v, v_fill);
+            dload(kp, kr.begin + t + 4, pg_k, k_fill);
         });
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(fa_vmcnt(BATCH));
@@ -867,13 +919,15 @@ fa_fwd_pp(const fa_kargs a) {
     if (n_tiles > 0) {
         // K(0) goes into buffer 3's K half (set 3 is not loaded before iteration 0's matrix
         // phase, after both groups have used K(0)); sets 0, 1, 2 into buffers 0, 1, 2.
-        dload(kp, kr.begin, lds_k3);
-        dload(vp, kr.begin, lds_v0);
-        dload(kp, kr.begin + 1, lds_k0);
-        dload(vp, kr.begin + 1, lds_v1);
-        dload(kp, kr.begin + 2, lds_k1);
-        dload(vp, kr.begin + 2, lds_v2);
-        dload(kp, kr.begin + 3, lds_k2);
+        const int pg0 = page_of(kr.begin), pg1 = page_of(kr.begin + 1);
+        const int pg2 = page_of(kr.begin + 2), pg3 = page_of(kr.begin + 3);
+        dload(kp, kr.begin, pg0, lds_k3);
+        dload(vp, kr.begin, pg0, lds_v0);
+        dload(kp, kr.begin + 1, pg1, lds_k0);
+        dload(vp, kr.begin + 1, pg1, lds_v1);
+        dload(kp, kr.begin + 2, pg2, lds_k1);
+        dload(vp, kr.begin + 2, pg2, lds_v2);
+        dload(kp, kr.begin + 3, pg3, lds_k2);
         __builtin_amdgcn_s_waitcnt(0);
         fa_lds_barrier();
         if (grp == 0) {
@@ -958,6 +1012,7 @@ __global__ __launch_bounds__(GN_BM) void fa_fwd_generic(const fa_kargs a, int de
     __shared__ float qs[GN_BM][DMAX + 1];
     __shared__ float ks[GN_BN][DMAX];
     __shared__ float vs[GN_BN][DMAX];
+    __shared__ int64_t roff[GN_BN];   // paged K / V: element offset of each key row of the tile
     const int tid = threadIdx.x;
     const int D = a.D;
     int b, h, qt;
@@ -987,15 +1042,33 @@ __global__ __launch_bounds__(GN_BM) void fa_fwd_generic(const fa_kargs a, int de
     const uint8_t* mrow = dense ? a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs
                                 : nullptr;
     float m = -INFINITY, l = 0.f;
+    const bool paged = a.block_table != nullptr;
+    const int32_t* bt = paged ? a.block_table + b * a.bt_stride : nullptr;
     for (int kt = kr.begin; kt < kr.end; ++kt) {
         const int j0 = kt * GN_BN;
         __syncthreads();   // previous tile fully consumed (and, first time, Q staged)
+        if (paged) {
+            // Key j lives in page bt[j / block_size], row j % block_size; -1 marks a row that
+            // reads as zeros (past Skv, or a page id outside the cache).
+            if (tid < GN_BN) {
+                const int j = j0 + tid;
+                int64_t o = -1;
+                if (j < g.skv) {
+                    const int pg = bt[j / a.block_size];
+                    if (unsigned(pg) < unsigned(a.num_pages))
+                        o = int64_t(pg) * a.page_stride + int64_t(j % a.block_size) * a.kv_rs;
+                }
+                roff[tid] = o;
+            }
+            __syncthreads();
+        }
         for (int e = tid; e < GN_BN * DMAX; e += GN_BM) {
             const int r = e / DMAX, d = e % DMAX;
             const int j = j0 + r;
-            const bool ok = j < g.skv && d < D;
-            ks[r][d] = ok ? to_f32(kp[int64_t(j) * a.kv_rs + d]) : 0.f;
-            vs[r][d] = ok ? to_f32(vp[int64_t(j) * a.kv_rs + d]) : 0.f;
+            const int64_t o = paged ? roff[r] : (j < g.skv ? int64_t(j) * a.kv_rs : -1);
+            const bool ok = o >= 0 && d < D;
+            ks[r][d] = ok ? to_f32(kp[o + d]) : 0.f;
+            vs[r][d] = ok ? to_f32(vp[o + d]) : 0.f;
         }
         __syncthreads();
         // One key at a time: running max m, running sum l, O rescaled when m grows.
@@ -1105,6 +1178,11 @@ fa_kargs make_kargs(const fa_plan& p, const void* q, const void* k, const void* 
     a.reverse_qt = p.reverse_qt;
     a.xcd_major = p.xcd_major;
     a.scale_log2 = scale * kLog2e;
+    a.page_stride = p.page_stride;
+    a.bt_stride = p.bt_stride;
+    a.block_size = p.block_size;
+    a.log2_block_size = p.log2_block_size;
+    a.num_pages = p.num_pages;
     return a;
 }
 
@@ -1157,6 +1235,94 @@ void launch_generic_t(const fa_kargs& a, int D, int alibi, bool dense, dim3 grid
     else fa_fwd_generic<T, 128><<<grid, block, 0, s>>>(a, dense, alibi);
 }
 
+template <int D, bool BF>
+void launch_pp_paged_d(const fa_kargs& a, int al, dim3 grid, hipStream_t s) {
+    const dim3 block(PP_THREADS);
+    switch (al) {
+        case 0: fa_fwd_pp<D, BF, 0, false, true><<<grid, block, 0, s>>>(a); break;
+        case 1: fa_fwd_pp<D, BF, 1, false, true><<<grid, block, 0, s>>>(a); break;
+        default: fa_fwd_pp<D, BF, 2, false, true><<<grid, block, 0, s>>>(a); break;
+    }
+}
+
+// Shared by fa_fwd and fa_fwd_paged: k / v are the tensors or the caches (block_table set).
+fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v, void* out, float* softmax_lse,
+                  const float* alibi_slopes, const uint8_t* atten_mask, const int32_t* block_table,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    fa_plan p;
+    fa_status st = fa_make_plan(c, true, &p);
+    if (st != FA_OK) return st;
+    if (!p.empty) {
+        if (!q || !out || !softmax_lse) return FA_ERR_NULLPTR;
+        if (p.kv_total > 0 && (!k || !v)) return FA_ERR_NULLPTR;
+        if (p.paged && p.kv_total > 0 && !block_table) return FA_ERR_NULLPTR;
+    }
+    if (p.ws_bytes > 0) {
+        if (!workspace) return FA_ERR_NULLPTR;
+        if (workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+    }
+    if (p.empty) return FA_OK;
+    const int64_t nblocks = p.n_items * p.N;
+    if (nblocks >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (log_enabled()) {
+        std::fprintf(stderr,
+                     "[fa] kernel=%s bm=%d bn=%d items/head=%lld blocks=%lld kv tiles visited/full/"
+                     "dense=%lld/%lld/%lld table=%d reverse=%d xcd_major=%d ws=%zu paged=%d\n",
+                     p.kernel == FA_KERNEL_PP ? "pingpong" : (p.kernel == FA_KERNEL_MFMA32 ? "mfma32" : "generic"),
+                     p.bm, p.bn,
+                     (long long)p.n_items, (long long)nblocks, (long long)p.kv_tiles_visited,
+                     (long long)p.kv_tiles_full, (long long)p.kv_tiles_total, int(p.table),
+                     p.reverse_qt, p.xcd_major, p.ws_bytes, int(p.paged));
+    }
+    st = upload_tables(p, workspace, s);
+    if (st != FA_OK) return st;
+    fa_kargs a = make_kargs(p, q, k, v, out, softmax_lse, alibi_slopes, atten_mask, workspace, c.scale);
+    a.alibi_left = c.alibi_mode == FA_ALIBI_LEFT ? 1 : 0;
+    a.block_table = p.paged ? block_table : nullptr;
+    const dim3 grid(static_cast<unsigned>(nblocks));
+    const int alibi = alibi_slopes == nullptr ? 0 : (c.alibi_mode == FA_ALIBI_SQRT ? 2 : 1);
+    const bool dense = c.sparse_mode == 1;
+    const int32_t dtype = c.dims->dtype;
+    (void)hipGetLastError();
+    if (p.kernel == FA_KERNEL_PP && p.paged) {
+        const bool bf = dtype == FA_DTYPE_BF16;
+        if (p.D == 128) {
+            if (bf) launch_pp_paged_d<128, true>(a, alibi, grid, s);
+            else launch_pp_paged_d<128, false>(a, alibi, grid, s);
+        } else {
+            if (bf) launch_pp_paged_d<64, true>(a, alibi, grid, s);
+            else launch_pp_paged_d<64, false>(a, alibi, grid, s);
+        }
+    } else if (p.kernel == FA_KERNEL_PP) {
+        const bool bf = dtype == FA_DTYPE_BF16;
+        if (p.D == 128) {
+            if (bf) launch_pp_d<128, true>(a, alibi, dense, grid, s);
+            else launch_pp_d<128, false>(a, alibi, dense, grid, s);
+        } else {
+            if (bf) launch_pp_d<64, true>(a, alibi, dense, grid, s);
+            else launch_pp_d<64, false>(a, alibi, dense, grid, s);
+        }
+    } else if (p.kernel == FA_KERNEL_MFMA32) {
+        const bool bf = dtype == FA_DTYPE_BF16;
+        if (p.D == 128) {
+            if (bf) launch_mfma32_d<128, true>(a, alibi, dense, grid, s);
+            else launch_mfma32_d<128, false>(a, alibi, dense, grid, s);
+        } else {
+            if (bf) launch_mfma32_d<64, true>(a, alibi, dense, grid, s);
+            else launch_mfma32_d<64, false>(a, alibi, dense, grid, s);
+        }
+    } else {
+        switch (dtype) {
+            case FA_DTYPE_F32: launch_generic_t<float>(a, p.D, alibi, dense, grid, s); break;
+            case FA_DTYPE_F16: launch_generic_t<_Float16>(a, p.D, alibi, dense, grid, s); break;
+            default: launch_generic_t<__bf16>(a, p.D, alibi, dense, grid, s); break;
+        }
+    }
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* out,
@@ -1180,66 +1346,35 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     c.has_mask = atten_mask != nullptr;
     c.mask_bcast = mask_bcast;
     c.scale = scale;
-    fa_plan p;
-    fa_status st = fa_make_plan(c, true, &p);
-    if (st != FA_OK) return st;
-    if (!p.empty) {
-        if (!q || !out || !softmax_lse) return FA_ERR_NULLPTR;
-        if (p.kv_total > 0 && (!k || !v)) return FA_ERR_NULLPTR;
-    }
-    if (p.ws_bytes > 0) {
-        if (!workspace) return FA_ERR_NULLPTR;
-        if (workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
-    }
-    if (p.empty) return FA_OK;
-    const int64_t nblocks = p.n_items * p.N;
-    if (nblocks >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (log_enabled()) {
-        std::fprintf(stderr,
-                     "[fa] kernel=%s bm=%d bn=%d items/head=%lld blocks=%lld kv tiles visited/full/"
-                     "dense=%lld/%lld/%lld table=%d reverse=%d xcd_major=%d ws=%zu\n",
-                     p.kernel == FA_KERNEL_PP ? "pingpong" : (p.kernel == FA_KERNEL_MFMA32 ? "mfma32" : "generic"),
-                     p.bm, p.bn,
-                     (long long)p.n_items, (long long)nblocks, (long long)p.kv_tiles_visited,
-                     (long long)p.kv_tiles_full, (long long)p.kv_tiles_total, int(p.table),
-                     p.reverse_qt, p.xcd_major, p.ws_bytes);
-    }
-    st = upload_tables(p, workspace, s);
-    if (st != FA_OK) return st;
-    fa_kargs a = make_kargs(p, q, k, v, out, softmax_lse, alibi_slopes, atten_mask, workspace, scale);
-    a.alibi_left = alibi_mode == FA_ALIBI_LEFT ? 1 : 0;
-    const dim3 grid(static_cast<unsigned>(nblocks));
-    const int alibi = alibi_slopes == nullptr ? 0 : (alibi_mode == FA_ALIBI_SQRT ? 2 : 1);
-    const bool dense = sparse_mode == 1;
-    (void)hipGetLastError();
-    if (p.kernel == FA_KERNEL_PP) {
-        const bool bf = dims->dtype == FA_DTYPE_BF16;
-        if (p.D == 128) {
-            if (bf) launch_pp_d<128, true>(a, alibi, dense, grid, s);
-            else launch_pp_d<128, false>(a, alibi, dense, grid, s);
-        } else {
-            if (bf) launch_pp_d<64, true>(a, alibi, dense, grid, s);
-            else launch_pp_d<64, false>(a, alibi, dense, grid, s);
-        }
-    } else if (p.kernel == FA_KERNEL_MFMA32) {
-        const bool bf = dims->dtype == FA_DTYPE_BF16;
-        if (p.D == 128) {
-            if (bf) launch_mfma32_d<128, true>(a, alibi, dense, grid, s);
-            else launch_mfma32_d<128, false>(a, alibi, dense, grid, s);
-        } else {
-            if (bf) launch_mfma32_d<64, true>(a, alibi, dense, grid, s);
-            else launch_mfma32_d<64, false>(a, alibi, dense, grid, s);
-        }
-    } else {
-        switch (dims->dtype) {
-            case FA_DTYPE_F32: launch_generic_t<float>(a, p.D, alibi, dense, grid, s); break;
-            case FA_DTYPE_F16: launch_generic_t<_Float16>(a, p.D, alibi, dense, grid, s); break;
-            default: launch_generic_t<__bf16>(a, p.D, alibi, dense, grid, s); break;
-        }
-    }
-    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-    return FA_OK;
+    return run_fwd(c, q, k, v, out, softmax_lse, alibi_slopes, atten_mask, nullptr, workspace, workspace_bytes,
+                   stream);
+}
+
+extern "C" fa_status fa_fwd_paged(const void* q, const void* key_cache, const void* value_cache, void* out,
+                                  float* softmax_lse, const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                                  int64_t pre_tokens, int64_t next_tokens, const int64_t* actual_seq_qlen,
+                                  const int64_t* actual_seq_kvlen, const int64_t* prefix,
+                                  const float* alibi_slopes, int32_t alibi_mode, const uint8_t* atten_mask,
+                                  const int64_t* mask_bcast, const fa_paged_kv* paged, float scale,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!paged) return FA_ERR_NULLPTR;
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = sparse_mode;
+    c.pre_tokens = pre_tokens;
+    c.next_tokens = next_tokens;
+    c.actual_seq_qlen = actual_seq_qlen;
+    c.actual_seq_kvlen = actual_seq_kvlen;
+    c.prefix = prefix;
+    c.has_alibi = alibi_slopes != nullptr;
+    c.alibi_mode = alibi_mode;
+    c.has_mask = atten_mask != nullptr;
+    c.mask_bcast = mask_bcast;
+    c.scale = scale;
+    c.paged = paged;
+    return run_fwd(c, q, key_cache, value_cache, out, softmax_lse, alibi_slopes, atten_mask, paged->block_table,
+                   workspace, workspace_bytes, stream);
 }
 
 extern "C" fa_status fa_mask_probe(const fa_dims* dims, int32_t layout, int32_t sparse_mode,

@@ -67,6 +67,18 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     }
     if (mode == 1 && tnd) return FA_ERR_UNSUPPORTED;
     if (d.D > 128) return FA_ERR_UNSUPPORTED;
+    const fa_paged_kv* pk = call.paged;
+    if (pk) {
+        if (pk->cache_layout != FA_CACHE_NORM && pk->cache_layout != FA_CACHE_NHSD) return FA_ERR_PARAM_INVALID;
+        if (pk->reserved != 0) return FA_ERR_PARAM_INVALID;
+        if (pk->block_size < 1 || pk->num_blocks < 1 || pk->max_blocks_per_seq < 1) return FA_ERR_PARAM_INVALID;
+        if (pk->block_size > (int64_t(1) << 24) || pk->num_blocks > INT32_MAX ||
+            pk->max_blocks_per_seq > (int64_t(1) << 24))
+            return FA_ERR_UNSUPPORTED;
+        // Cache elements (and so every page offset) must stay well inside int64.
+        if (double(pk->num_blocks) * double(pk->block_size) * double(d.N) * double(d.D) > std::ldexp(1.0, 60))
+            return FA_ERR_UNSUPPORTED;
+    }
 
     const int64_t B = d.B;
     std::vector<int64_t> sq(B), skv(B), qs(B), ks(B);
@@ -108,6 +120,8 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         max_sq = std::max(max_sq, sq[b]);
         max_skv = std::max(max_skv, skv[b]);
     }
+    // The block table must reach the last key of the longest sequence.
+    if (pk && max_skv > pk->max_blocks_per_seq * pk->block_size) return FA_ERR_PARAM_INVALID;
 
     // Mode-specific arguments.
     const int64_t pre = call.pre_tokens, nxt = call.next_tokens;
@@ -157,7 +171,18 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     p.kernel = FA_KERNEL_GENERIC;
     p.bm = FA_GEN_BM;
     p.bn = FA_GEN_BN;
-    if (mfma_eligible(d.dtype, d.N, d.D)) {
+    if (pk) {
+        // Paged K / V: the ping-pong kernel when its tiles fit whole pages and the page ids
+        // fit its LDS table, else the generic kernel (any block size, explicit masks too).
+        const int64_t bs = pk->block_size;
+        const bool pow2 = (bs & (bs - 1)) == 0;
+        if (mfma_eligible(d.dtype, d.N, d.D) && mode != 1 && pow2 && bs >= FA_PP_BN &&
+            ceil_div(max_skv, bs) <= FA_PP_MAX_PAGES) {
+            p.kernel = FA_KERNEL_PP;
+            p.bm = FA_PP_BM;
+            p.bn = FA_PP_BN;
+        }
+    } else if (mfma_eligible(d.dtype, d.N, d.D)) {
         if (!prefer_mfma32()) {
             p.kernel = FA_KERNEL_PP;
             p.bm = FA_PP_BM;
@@ -181,7 +206,7 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     for (int64_t b = 0; b < B; ++b) {
         fa_geom g{};
         g.q_start = int32_t(qs[b]);
-        g.kv_start = int32_t(ks[b]);
+        g.kv_start = pk ? 0 : int32_t(ks[b]);   // a paged sequence starts at key 0 of its pages
         g.sq = int32_t(sq[b]);
         g.skv = int32_t(skv[b]);
         const int32_t off = g.skv - g.sq;
@@ -218,6 +243,23 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     } else {
         p.q_bs = 0; p.q_hs = D; p.q_rs = N * D;
         p.kv_bs = 0; p.kv_hs = D; p.kv_rs = N * D;
+    }
+    if (pk) {
+        const int64_t bs = pk->block_size;
+        p.paged = true;
+        p.kv_bs = 0;
+        if (pk->cache_layout == FA_CACHE_NORM) {   // [num_blocks, block_size, N, D]
+            p.page_stride = bs * N * D; p.kv_hs = D; p.kv_rs = N * D;
+        } else {                                   // [num_blocks, N, block_size, D]
+            p.page_stride = N * bs * D; p.kv_hs = bs * D; p.kv_rs = D;
+        }
+        p.bt_stride = pk->max_blocks_per_seq;
+        p.block_size = int32_t(bs);
+        p.log2_block_size = -1;
+        if ((bs & (bs - 1)) == 0)
+            for (int32_t e = 0; e < 31; ++e)
+                if ((int64_t(1) << e) == bs) p.log2_block_size = e;
+        p.num_pages = int32_t(pk->num_blocks);
     }
     if (tnd) {
         p.lse_bs = 0; p.lse_hs = d.T_q;
@@ -336,6 +378,25 @@ extern "C" fa_status fa_fwd_workspace_size(const fa_dims* dims, int32_t layout,
     c.sparse_mode = sparse_mode;
     c.actual_seq_qlen = actual_seq_qlen;
     c.actual_seq_kvlen = actual_seq_kvlen;
+    fa_plan p;
+    const fa_status st = fa_make_plan_sizes(c, &p);
+    if (st != FA_OK) return st;
+    *bytes = p.ws_bytes;
+    return FA_OK;
+}
+
+extern "C" fa_status fa_fwd_paged_workspace_size(const fa_dims* dims, int32_t layout,
+                                                 int32_t sparse_mode, const int64_t* actual_seq_qlen,
+                                                 const int64_t* actual_seq_kvlen,
+                                                 const fa_paged_kv* paged, size_t* bytes) {
+    if (!dims || !bytes || !paged) return FA_ERR_NULLPTR;
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = sparse_mode;
+    c.actual_seq_qlen = actual_seq_qlen;
+    c.actual_seq_kvlen = actual_seq_kvlen;
+    c.paged = paged;
     fa_plan p;
     const fa_status st = fa_make_plan_sizes(c, &p);
     if (st != FA_OK) return st;

@@ -27,6 +27,7 @@ struct fa_call {
     const int64_t* mask_bcast = nullptr;
     float scale = 1.0f;
     bool check_scale = true;
+    const fa_paged_kv* paged = nullptr;   // K / V read from paged caches (fa_fwd_paged)
 };
 
 // Kernel families and their tiles.
@@ -37,6 +38,9 @@ constexpr int FA_MFMA32_BM = 128;   // 4 waves x 32 rows
 constexpr int FA_MFMA32_BN = 64;
 constexpr int FA_GEN_BM = 64;
 constexpr int FA_GEN_BN = 16;
+// Paged K / V in the ping-pong kernel: pages of a power-of-two size >= 64 (a 64-key tile never
+// straddles two pages) and at most this many pages per sequence (their ids are staged in LDS).
+constexpr int FA_PP_MAX_PAGES = 2048;
 
 struct fa_plan {
     int32_t kernel = FA_KERNEL_GENERIC;
@@ -63,6 +67,13 @@ struct fa_plan {
     int64_t kv_bs = 0, kv_hs = 0, kv_rs = 0;
     int64_t lse_bs = 0, lse_hs = 0;
     int64_t m_bs = 0, m_hs = 0, m_rs = 0;
+    // Paged K / V (kv_bs is 0 and every sequence starts at key 0 of its own pages).
+    bool paged = false;
+    int64_t page_stride = 0;    // elements from one page to the next
+    int64_t bt_stride = 0;      // block_table row length
+    int32_t block_size = 0;
+    int32_t log2_block_size = -1;   // -1 unless block_size is a power of two
+    int32_t num_pages = 0;
     // Statistics (per head).
     int64_t kv_tiles_visited = 0, kv_tiles_full = 0, kv_tiles_total = 0;
 };

@@ -334,3 +334,68 @@ def test_scatter_kv_cache_validation(lib):
     assert call(dims(num_tokens=-1)) == INVALID
     assert call(dims(num_tokens=0), key=None, val=None, kc=None, vc=None, slots=None) == OK
     assert call(dims(num_heads=1 << 17)) == UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------------------
+# Paged forward: host validation of the block-table description (no device work)
+# ---------------------------------------------------------------------------------------
+
+def test_fwd_paged_validation(lib):
+    """fa_fwd_paged checks its fa_paged_kv before any launch: layout, reserved field, sizes,
+    a block table long enough for the longest sequence, and the pointers it needs."""
+    buf = (ctypes.c_char * 4096)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    d = bnsd(B=2, N=4, Sq=64, Skv=300, D=128)
+
+    def pk(**kw):
+        base = dict(block_table=p.value, max_blocks_per_seq=3, num_blocks=8, block_size=128, cache_layout=0,
+                    reserved=0)
+        base.update(kw)
+        return fb.FaPagedKv(**base)
+
+    def call(paged, dims=d, mode=3, kc=p, vc=p):
+        return lib.fa_fwd_paged(p, kc, vc, p, p, ctypes.byref(dims), 0, mode, 0, 0, None, None, None, None, 0,
+                                None, None, ctypes.byref(paged) if paged is not None else None, 0.125, None, 0,
+                                None)
+
+    assert call(None) == NULLPTR
+    assert call(pk(cache_layout=2)) == INVALID
+    assert call(pk(cache_layout=-1)) == INVALID
+    assert call(pk(reserved=1)) == INVALID
+    assert call(pk(block_size=0)) == INVALID
+    assert call(pk(num_blocks=0)) == INVALID
+    assert call(pk(max_blocks_per_seq=0)) == INVALID
+    assert call(pk(max_blocks_per_seq=2)) == INVALID        # 2 pages x 128 keys < 300 keys
+    assert call(pk(block_size=64, max_blocks_per_seq=4)) == INVALID
+    assert call(pk(num_blocks=1 << 32)) == UNSUPPORTED
+    assert call(pk(block_table=None)) == NULLPTR
+    assert call(pk(), kc=None) == NULLPTR
+    assert call(pk(), vc=None) == NULLPTR
+    assert call(pk(), mode=9) == INVALID                    # fa_fwd's own rules still hold
+    # no keys anywhere: nothing is read, so no table is needed
+    d0 = bnsd(B=2, N=4, Sq=64, Skv=0, D=128)
+    ws_sz = ctypes.c_size_t(0)
+    assert lib.fa_fwd_paged_workspace_size(ctypes.byref(d0), 0, 3, None, None, ctypes.byref(pk()),
+                                           ctypes.byref(ws_sz)) == OK
+    assert lib.fa_fwd_paged_workspace_size(ctypes.byref(d), 0, 3, None, None, None, ctypes.byref(ws_sz)) == NULLPTR
+    assert lib.fa_fwd_paged_workspace_size(ctypes.byref(d), 0, 3, None, None, ctypes.byref(pk(reserved=2)),
+                                           ctypes.byref(ws_sz)) == INVALID
+
+
+def test_fwd_paged_workspace_follows_page_size(lib):
+    """Pages of 128 keys keep the 256-row ping-pong tiles (the same workspace as fa_fwd); pages
+    of 16 keys fall back to the generic kernel's 64-row tiles, whose work list is longer."""
+    buf = (ctypes.c_char * 4096)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    dt = tnd([300, 7], [300, 9])
+    qc, kc = [300, 307], [300, 309]
+    big = fb.FaPagedKv(p.value, 3, 8, 128, 0, 0)
+    small = fb.FaPagedKv(p.value, 19, 64, 16, 1, 0)
+    w128 = fb.fa_fwd_paged_workspace_size(dt, "TND", 3, big, qc, kc)
+    w16 = fb.fa_fwd_paged_workspace_size(dt, "TND", 3, small, qc, kc)
+    assert w128 == fb.fa_fwd_workspace_size(dt, "TND", 3, qc, kc)
+    # items (batch, q tile), 8 bytes each: 2 + 1 with 256-row tiles, 5 + 1 with 64-row tiles
+    assert w16 - w128 == (6 - 3) * 8
+    st = lib.fa_fwd_paged(p, p, p, p, p, ctypes.byref(dt), 2, 3, 0, 0, fb._i64(qc), fb._i64(kc), None, None, 0,
+                          None, None, ctypes.byref(small), 0.125, p, w16 - 1, None)
+    assert st == WORKSPACE
