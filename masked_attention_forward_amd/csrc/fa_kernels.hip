@@ -611,8 +611,6 @@ fa_fwd_pp(const fa_kargs a) {
 
     __shared__ u32x4 lds_k0[TILE_CHUNKS], lds_k1[TILE_CHUNKS], lds_k2[TILE_CHUNKS], lds_k3[TILE_CHUNKS];
     __shared__ u32x4 lds_v0[TILE_CHUNKS], lds_v1[TILE_CHUNKS], lds_v2[TILE_CHUNKS], lds_v3[TILE_CHUNKS];
-    // Paged K / V: ids of the pages this item's key range touches, first page first.
-    __shared__ int32_t lds_pages[PAGED ? FA_PP_MAX_PAGES : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -663,35 +661,34 @@ fa_fwd_pp(const fa_kargs a) {
     const uint8_t* mrow = nullptr;
     if (DENSE) mrow = a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs;
 
-    // Paged K / V: a 64-key tile lies inside one page (pages hold 2^lbs >= 64 keys). The ids of
-    // pages pg_first .. (kv_lim - 1) >> lbs go to LDS once; a tile's id is read from there one
-    // phase before its load, so no scalar memory load (and its full lgkmcnt wait) sits in the
-    // loop.
-    int lbs = 0, pg_first = 0, n_pages = 0;
-    int64_t pg_stride = 0;
+    // Paged K / V: a 64-key tile lies inside one page (pages hold 2^lbs >= 64 keys). Page ids
+    // come straight from the block table with scalar loads, issued at the start of a softmax
+    // phase and landed before its closing LDS reads: no VALU work (which would compete with the
+    // other group's softmax on the same SIMD) and no wait inside a matrix phase.
+    // (The table is read through the constant address space: it does not change during the
+    // kernel, and uniform loads from there are scalar.)
+    int lbs = 0, n_pages = 0, pg_last = 0, bs_mask = 0;
+    uint32_t pg_bytes = 0;
+    const __attribute__((address_space(4))) int32_t* bt_row = nullptr;
     if constexpr (PAGED) {
         lbs = a.log2_block_size;
+        bs_mask = (1 << lbs) - 1;
         n_pages = a.num_pages;
-        pg_stride = a.page_stride;
-        asm volatile("" : : "s"(lbs), "s"(n_pages), "s"(pg_stride));
-        if (n_tiles > 0) {
-            pg_first = (kr.begin * BN) >> lbs;
-            const int cnt = ((kv_lim - 1) >> lbs) - pg_first + 1;
-            const int32_t* bt = a.block_table + b * a.bt_stride + pg_first;
-            for (int e = tid; e < cnt; e += NT) lds_pages[e] = bt[e];
-        }
-        __syncthreads();
+        pg_bytes = uint32_t(a.page_stride) * 2u;
+        bt_row = (const __attribute__((address_space(4))) int32_t*)(a.block_table + b * a.bt_stride);
+        pg_last = n_tiles > 0 ? (kv_lim - 1) >> lbs : 0;   // last table entry this item reads
+        asm volatile("" : : "s"(lbs), "s"(n_pages), "s"(pg_bytes), "s"(bs_mask));
     }
     // Page id of key tile kt (-1 past the item's range: that load reads nothing).
     auto page_of = [&](int kt) __attribute__((always_inline)) {
         if constexpr (PAGED) {
-            const int e = min(max(((kt * BN) >> lbs) - pg_first, 0), FA_PP_MAX_PAGES - 1);
-            const int pg = fa_uniform(lds_pages[e]);
+            const int pg = bt_row[min((kt * BN) >> lbs, pg_last)];
             return kt < kr.end ? pg : -1;
         } else {
             return 0;
         }
     };
+    int pg_v_next = 0, pg_k_next = 0;   // page ids of the next iteration's V and K loads
 
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -714,8 +711,12 @@ fa_fwd_pp(const fa_kargs a) {
         int rows = min(BN, kv_lim - j0);
         const uint16_t* tile = base + int64_t(j0) * kv_rs;
         if constexpr (PAGED) {
+            // Page bytes and in-page offsets fit 32 bits (checked on the host): one 32 x 32 -> 64
+            // bit product per tile.
             rows = unsigned(page) < unsigned(n_pages) ? rows : 0;
-            tile = base + int64_t(page) * pg_stride + int64_t(j0 & ((1 << lbs) - 1)) * kv_rs;
+            tile = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) +
+                                                     uint64_t(uint32_t(page)) * pg_bytes +
+                                                     uint32_t((j0 & bs_mask) * kv_rs) * 2u);
         }
         const __amdgpu_buffer_rsrc_t r = fa_rsrc(tile, rows > 0 ? ((rows - 1) * kv_rs + D) * 2 : 0);
 #pragma unroll
@@ -876,14 +877,23 @@ fa_fwd_pp(const fa_kargs a) {
         between();
         qk(kb);
         // LDS reads run about three MFMAs ahead: two per PV MFMA (its two V^T halves) and one
-        // per S^T MFMA.
+        // per S^T MFMA. The tile loads of `between` (scalar address arithmetic, M0 and the DMA
+        // issue) go into the gaps of the first MFMAs: left free, the scheduler puts them all
+        // ahead of the first MFMA, which then starts late.
         constexpr int NPV = 4 * DBLK, NQK = 2 * KSTEPS;
+        constexpr int NDMA = 2 * LOADS;
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
         for (int i = 0; i < NPV + NQK; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i < 16) __builtin_amdgcn_sched_group_barrier(0x004, 4, 0);
+            // V tile after MFMAs 5.., K tile after MFMAs 11..: each address chain has a few
+            // MFMA gaps to run in.
+#pragma unroll
+            for (int p = 0; p < NDMA; ++p)
+                if (i == 5 + 6 * (p / LOADS) + p % LOADS) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
         }
     };
 
@@ -902,8 +912,15 @@ fa_fwd_pp(const fa_kargs a) {
         const u32x4* v_cur = S == 0 ? lds_v0 : (S == 1 ? lds_v1 : (S == 2 ? lds_v2 : lds_v3));
         u32x4* k_fill = F == 0 ? lds_k0 : (F == 1 ? lds_k1 : (F == 2 ? lds_k2 : lds_k3));
         u32x4* v_fill = F == 0 ? lds_v0 : (F == 1 ? lds_v1 : (F == 2 ? lds_v2 : lds_v3));
-        const int pg_v = page_of(kr.begin + t + 3), pg_k = page_of(kr.begin + t + 4);
+        // Page ids of this iteration's loads were fetched one iteration ago; fetch the next ones.
+        const int pg_v = pg_v_next, pg_k = pg_k_next;
+        if constexpr (PAGED) {
+            pg_v_next = page_of(kr.begin + t + 4);
+            pg_k_next = page_of(kr.begin + t + 5);
+        }
         softmax(t);
+        // The scalar loads land here, while no LDS read is in flight.
+        if constexpr (PAGED) asm volatile("" : : "s"(pg_v_next), "s"(pg_k_next));
         prefetch(v_cur);
         fa_lds_barrier_pending<2 * NPRE>();   // the prefetched V^T reads may still be in flight
         __builtin_amdgcn_s_setprio(1);
@@ -921,6 +938,8 @@ fa_fwd_pp(const fa_kargs a) {
         // phase, after both groups have used K(0)); sets 0, 1, 2 into buffers 0, 1, 2.
         const int pg0 = page_of(kr.begin), pg1 = page_of(kr.begin + 1);
         const int pg2 = page_of(kr.begin + 2), pg3 = page_of(kr.begin + 3);
+        pg_v_next = pg3;
+        pg_k_next = page_of(kr.begin + 4);
         dload(kp, kr.begin, pg0, lds_k3);
         dload(vp, kr.begin, pg0, lds_v0);
         dload(kp, kr.begin + 1, pg1, lds_k0);

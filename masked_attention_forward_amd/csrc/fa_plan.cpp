@@ -172,12 +172,14 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     p.bm = FA_GEN_BM;
     p.bn = FA_GEN_BN;
     if (pk) {
-        // Paged K / V: the ping-pong kernel when its tiles fit whole pages and the page ids
-        // fit its LDS table, else the generic kernel (any block size, explicit masks too).
+        // Paged K / V: the ping-pong kernel when its tiles fit whole pages, a sequence has at
+        // most FA_PP_MAX_PAGES pages and a page is under 4 GiB; else the generic kernel (any
+        // block size, explicit masks too).
         const int64_t bs = pk->block_size;
         const bool pow2 = (bs & (bs - 1)) == 0;
+        const int64_t page_bytes = bs * d.N * d.D * 2;
         if (mfma_eligible(d.dtype, d.N, d.D) && mode != 1 && pow2 && bs >= FA_PP_BN &&
-            ceil_div(max_skv, bs) <= FA_PP_MAX_PAGES) {
+            ceil_div(max_skv, bs) <= FA_PP_MAX_PAGES && page_bytes < (int64_t(1) << 32)) {
             p.kernel = FA_KERNEL_PP;
             p.bm = FA_PP_BM;
             p.bn = FA_PP_BN;

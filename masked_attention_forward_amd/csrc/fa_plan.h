@@ -39,7 +39,7 @@ constexpr int FA_MFMA32_BN = 64;
 constexpr int FA_GEN_BM = 64;
 constexpr int FA_GEN_BN = 16;
 // Paged K / V in the ping-pong kernel: pages of a power-of-two size >= 64 (a 64-key tile never
-// straddles two pages) and at most this many pages per sequence (their ids are staged in LDS).
+// straddles two pages) and at most this many pages per sequence.
 constexpr int FA_PP_MAX_PAGES = 2048;
 
 struct fa_plan {
