@@ -37,11 +37,15 @@ DOMINANT_KERNEL = "fa_fwd_pp"
 METRIC = "effective TFLOP/s (unmasked FLOPs) attn fwd bf16 D=128; % of MFMA peak"
 
 
-def kernel_sources_sha() -> str:
-    """Hash of the code lines of KERNEL_SOURCES (full-line comments and blank lines skipped, so
-    a comment edit does not invalidate recorded counters; any code change does)."""
+SCATTER_SOURCES = ["masked_attention_forward_amd/csrc/fa_kv_cache.hip"]
+
+
+def kernel_sources_sha(sources=None) -> str:
+    """Hash of the code lines of `sources` (KERNEL_SOURCES by default; full-line comments and
+    blank lines skipped, so a comment edit does not invalidate recorded counters; any code
+    change does)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             for line in f:
                 t = line.strip()
@@ -50,10 +54,10 @@ def kernel_sources_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, path=None, sources=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"{DOMINANT_KERNEL}_{workload}_counters.md")
+    path = path or os.path.join(ROOT, "profiles", f"{DOMINANT_KERNEL}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -62,7 +66,7 @@ def recorded_traffic(workload: str):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_sources_sha256") != kernel_sources_sha():
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha(sources):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -199,7 +203,11 @@ def bench_scatter(args, dev):
         "config": {"workload": "kv_scatter_prefill", "num_tokens": T, "N": N, "D": D, "num_blocks": nb,
                    "block_size": bs, "layout": "Norm"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "algorithmic_bytes": moved}}),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": recorded_traffic("kv_scatter_prefill",
+                                                 os.path.join(ROOT, "profiles", "fa_kv_scatter_prefill_trace.md"),
+                                                 SCATTER_SOURCES),
+                     "algorithmic_bytes": moved, "kernel_sources_sha256": kernel_sources_sha(SCATTER_SOURCES)}}),
           flush=True)
 
 
