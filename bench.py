@@ -35,6 +35,7 @@ KERNEL_SOURCES = ["masked_attention_forward_amd/csrc/fa_kernels.hip",
                   "masked_attention_forward_amd/csrc/fa_plan.h"]
 DOMINANT_KERNEL = "fa_fwd_pp"
 METRIC = "effective TFLOP/s (unmasked FLOPs) attn fwd bf16 D=128; % of MFMA peak"
+DECODE_METRIC = "effective HBM GB/s attn decode (Q, K, V read once, O and LSE written once)"
 
 
 SCATTER_SOURCES = ["masked_attention_forward_amd/csrc/fa_kv_cache.hip"]
@@ -94,8 +95,9 @@ def visible_pairs(w, dev) -> int:
     return total
 
 
-def cpu_baseline(w, heads: int):
-    """Time the fp64 oracle on `heads` whole (batch, head) slices of the workload."""
+def cpu_baseline(w, heads: int, decode: bool = False):
+    """Time the fp64 oracle on `heads` whole (batch, head) slices of the workload (TFLOP/s, or
+    algorithmic GB/s for a decode workload)."""
     import numpy as np
     import oracle
     try:
@@ -123,7 +125,13 @@ def cpu_baseline(w, heads: int):
                                     next_tokens=w.next_tokens,
                                     prefix_len=prefix[0] if prefix else 0)
         flops += 4 * w.D * int(vis.sum())
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    if decode:
+        elem = q.element_size()
+        moved = len(sel) * ((2 * w.Sq * w.D + 2 * w.Skv * w.D) * elem + 4 * w.Sq)
+        value, unit = moved / t_total / 1e9, "GB/s"
+    else:
+        value, unit = flops / t_total / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": int(threads),
             "kind": "oracle",
             "sample": f"{len(sel)} of {w.B * w.N} (batch, head) slices at full Sq={w.Sq}, Skv={w.Skv}; "
                       f"{t_total:.1f} s of fp64 numpy (BLAS threads={threads}, elementwise on 1 core)"}
@@ -303,11 +311,14 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = recorded_traffic(args.workload) if paged is None else None
+    # At most 16 query rows per sequence: the split-KV decode path, bound by HBM.
+    decode = max(w.qlens) <= 16 if w.layout == "TND" else w.Sq <= 16
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
 
     res = {
-        "metric": METRIC,
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
+        "metric": DECODE_METRIC if decode else METRIC,
+        "value": round(gbs if decode else tflops, 2),
+        "unit": "GB/s" if decode else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -330,8 +341,13 @@ def main():
                      "algorithmic_bytes": alg_bytes,
                      "kernel_sources_sha256": kernel_sources_sha()},
     }
+    if decode:
+        res["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                           "algorithmic_bytes": alg_bytes, "kernel_sources_sha256": kernel_sources_sha()}
+        res["config"]["effective_tflops"] = round(tflops, 3)
     if not args.no_cpu_baseline and w.layout == "BNSD":
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads, decode)
     print(json.dumps(res), flush=True)
 
 

@@ -80,6 +80,7 @@ struct fa_kargs {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -1007,6 +1008,349 @@ fa_fwd_pp(const fa_kargs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Split-KV decode: at most 16 query rows per (batch, head). One workgroup per (batch, head,
+// split of the visible kv tiles); its four waves take every fourth tile of the split, each
+// with its own online-softmax state, and combine at the end; fa_decode_merge combines the
+// splits with LSE = log2-sum-exp2 of the split LSEs and O = sum of 2^(LSE_s - LSE) O_s.
+//
+// MFMA 16x16x32: S^T = K Q^T with K as the A operand straight from HBM (16 bytes per lane,
+// rows past the tile's valid keys read as zeros) and the query rows as the 16 columns. Key
+// rows are permuted inside the 64-key tile so that each lane's S^T values are exactly its P
+// operand of O = P V (rows: queries, k: keys): block bb, A row r holds key
+// 32 (bb / 2) + 8 (r / 4) + 4 (bb % 2) + r % 4. V goes to a per-wave LDS buffer with direct
+// loads and comes back as the B operand (8 consecutive keys of one column per lane) through
+// ds_read_b64_tr_b16, whose 16-lane groups return element i % 4 of the vector addressed by
+// lane 4 e + i / 4 as element e of lane i.
+// ------------------------------------------------------------------------------------------
+
+constexpr int DC_THREADS = 256;
+constexpr int DC_BN = FA_DEC_BN;     // keys per tile
+constexpr int DC_ROWS = FA_DEC_ROWS; // query rows (the MFMA's 16 columns)
+
+// s_waitcnt immediate for vmcnt(n), n < 64 (vmcnt bits 3:0 and 15:14; the other counters
+// left at their maxima).
+constexpr int fa_vmcnt64(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <bool IS_BF16>
+struct mfma16_io;
+
+template <>
+struct mfma16_io<true> {
+    static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <>
+struct mfma16_io<false> {
+    static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
+
+struct fa_decode_args {
+    float* o_part;     // [B N n_split, 16, D]: each split's O / l (n_split > 1)
+    float* lse_part;   // [B N n_split, 16]: each split's log2(sum) + max, log2 domain
+    int32_t n_split;
+};
+
+template <int D, bool IS_BF16, int AL, bool PAGED>
+__global__ __launch_bounds__(DC_THREADS) void fa_decode_split(const fa_kargs a, const fa_decode_args dc) {
+    static_assert(D == 64 || D == 128, "MFMA decode covers D = 64 and 128");
+    using io = mfma_io<IS_BF16>;
+    using mm = mfma16_io<IS_BF16>;
+    constexpr int KD = D / 32;                 // k-steps of S^T = K Q^T
+    constexpr int NK = 4 * KD;                 // K operand loads per tile (4 blocks of 16 keys)
+    constexpr int ROW_B = D * 2;               // bytes of a key row
+    constexpr int NV = DC_BN * ROW_B / 1024;   // 1 KB direct loads per V tile
+    constexpr int RPL = 1024 / ROW_B;          // V rows per direct load
+    constexpr int DB = D / 16;                 // 16-column blocks of O
+    constexpr int TILE_U4 = DC_BN * D / 8;     // 16-byte chunks of a tile
+    __shared__ u32x4 lds_v[4 * 2 * TILE_U4];   // per wave, two V tiles
+
+    const int lane = threadIdx.x & 63;
+    const int wave = fa_uniform(threadIdx.x >> 6);
+    const int n = lane & 15;    // query row (S^T column / P and O row block index)
+    const int gq = lane >> 4;   // 16-lane group
+
+    const int w = blockIdx.x;
+    const int split = w % dc.n_split;
+    const int bh = w / dc.n_split;
+    const int h = bh % a.N, b = bh / a.N;
+    const fa_geom g = fa_geom_of(a, b);
+    if (g.sq <= 0) return;
+    const int rows = min(g.sq, DC_ROWS);
+    const fa_kv_range kr = fa_tile_kv_range(g, 0, rows - 1, DC_BN);
+    const int n_tiles = kr.end - kr.begin;
+    const int tps = (n_tiles + dc.n_split - 1) / dc.n_split;
+    const int t0 = min(kr.begin + split * tps, kr.end);
+    const int t1 = min(t0 + tps, kr.end);
+    const int kv_lim = min(kr.end * DC_BN, g.skv);
+
+    const int q_rs = int(a.q_rs), kv_rs = int(a.kv_rs);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + h * a.q_hs + int64_t(g.q_start) * a.q_rs;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+
+    // Q^T operand: lane (gq, n) holds query row n, columns 32 kd + 8 gq .. + 7 (rows past Sq
+    // read as zeros: their offsets are past the buffer's end because q_rs >= D).
+    u32x4 qop[KD];
+    {
+        const __amdgpu_buffer_rsrc_t rq = fa_rsrc(qp, ((rows - 1) * q_rs + D) * 2);
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd) qop[kd] = fa_bload(rq, (n * q_rs + 32 * kd + 8 * gq) * 2);
+    }
+    const int row_lo = fa_row_lo(g, n), row_hi = fa_row_hi(g, n);
+    const float sl2 = a.scale_log2;
+    float slope2 = 0.f;
+    if (AL != 0) slope2 = a.slopes[h] * kLog2e;
+    const int off = g.skv - g.sq;
+    const int aoff = a.alibi_left ? 0 : off;
+
+    // Paged K / V: page ids by scalar loads (the table is read-only during the kernel).
+    int lbs = 0, n_pages = 0, bs_mask = 0, pg_last = 0;
+    uint32_t pg_bytes = 0;
+    const __attribute__((address_space(4))) int32_t* bt_row = nullptr;
+    if constexpr (PAGED) {
+        lbs = a.log2_block_size;
+        bs_mask = (1 << lbs) - 1;
+        n_pages = a.num_pages;
+        pg_bytes = uint32_t(a.page_stride) * 2u;
+        bt_row = (const __attribute__((address_space(4))) int32_t*)(a.block_table + b * a.bt_stride);
+        pg_last = n_tiles > 0 ? (kv_lim - 1) >> lbs : 0;
+    }
+
+    // Per-lane operand offsets.
+    int k_off[4][KD];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+        const int key = 32 * (bb >> 1) + 8 * (n >> 2) + 4 * (bb & 1) + (n & 3);
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd) k_off[bb][kd] = (key * kv_rs + 32 * kd + 8 * gq) * 2;
+    }
+    const int v_voff = (lane * 16 / ROW_B) * kv_rs * 2 + (lane * 16) % ROW_B;
+    int v_tr[2][2];   // [kk][half]: byte address in the tile of this lane's transpose read (column block 0)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) v_tr[kk][hf] = (32 * kk + 8 * gq + 4 * hf + (n >> 2)) * ROW_B + 8 * (n & 3);
+
+    u32x4 kreg[2][NK];
+    char* const vbuf = reinterpret_cast<char*>(lds_v) + wave * 2 * TILE_U4 * 16;
+
+    // Loads of tile t into buffer BUF (t >= t1: nothing read, zeros written).
+    auto issue = [&](auto buf_tag, int t) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        const int j0 = t * DC_BN;
+        int nrows = t < t1 ? min(DC_BN, kv_lim - j0) : 0;
+        const uint16_t* kt = kp + int64_t(j0) * kv_rs;
+        const uint16_t* vt = vp + int64_t(j0) * kv_rs;
+        if constexpr (PAGED) {
+            const int pg = bt_row[min(j0 >> lbs, pg_last)];
+            nrows = unsigned(pg) < unsigned(n_pages) ? nrows : 0;
+            const uint64_t o = uint64_t(uint32_t(pg)) * pg_bytes + uint32_t((j0 & bs_mask) * kv_rs) * 2u;
+            kt = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(kp) + o);
+            vt = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(vp) + o);
+        }
+        const int bytes = nrows > 0 ? ((nrows - 1) * kv_rs + D) * 2 : 0;
+        const __amdgpu_buffer_rsrc_t rk = fa_rsrc(kt, bytes), rv = fa_rsrc(vt, bytes);
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int kd = 0; kd < KD; ++kd) kreg[BUF][bb * KD + kd] = fa_bload(rk, k_off[bb][kd]);
+#pragma unroll
+        for (int p = 0; p < NV; ++p)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vbuf + (BUF * TILE_U4 + p * 64) * 16), 16,
+                                                     v_voff + p * RPL * kv_rs * 2, 0, 0, 0);
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x4{};
+
+    auto compute = [&](auto buf_tag, int t) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        const int j0 = t * DC_BN;
+        f32x4 sacc[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            sacc[bb] = f32x4{};
+#pragma unroll
+            for (int kd = 0; kd < KD; ++kd) sacc[bb] = mm::mma(kreg[BUF][bb * KD + kd], qop[kd], sacc[bb]);
+        }
+        // Value (bb, e) of this lane: query row n, key j0 + 32 (bb / 2) + 8 gq + 4 (bb % 2) + e.
+        const bool full = fa_tile_full(g, 0, rows - 1, j0, DC_BN);
+        float sv[16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 32 * (bb >> 1) + 8 * gq + 4 * (bb & 1) + e;
+                float x = sacc[bb][e] * sl2;
+                if (AL == 1) x = fmaf(slope2, float(j - n - aoff), x);
+                if (AL == 2) {
+                    const float dd = float(n + off - j);
+                    x -= slope2 * copysignf(__builtin_amdgcn_sqrtf(fabsf(dd)), dd);
+                }
+                if (!full) x = (j >= row_lo && j <= row_hi) ? x : -INFINITY;
+                sv[4 * bb + e] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // Rescale only when the row maximum grows by more than 2^8 (as in the forward kernels).
+        const bool need = mx > m_run + 8.f;
+        const float alpha = need ? exp2f(m_run - mx) : 1.f;
+        m_run = need ? mx : m_run;
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float p[16];
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
+            ls += p[i];
+        }
+        l_run = fmaf(l_run, alpha, ls);
+        if (__any(need)) {
+            // O rows are 4 gq + e: their factors live in lanes 4 gq + e.
+            float ar[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, 4 * gq + e);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oacc[db][e] *= ar[e];
+        }
+        u32x4 pop[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const float* lo = p + 8 * kk;   // block 2 kk: keys 32 kk + 8 gq + 0..3
+            const float* hi = p + 8 * kk + 4;   // block 2 kk + 1: keys 32 kk + 8 gq + 4..7
+            pop[kk] = u32x4{io::pack(lo[0], lo[1]), io::pack(lo[2], lo[3]), io::pack(hi[0], hi[1]),
+                            io::pack(hi[2], hi[3])};
+        }
+        const char* vb = vbuf + BUF * TILE_U4 * 16;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vb + v_tr[kk][0] + 32 * db));
+                const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vb + v_tr[kk][1] + 32 * db));
+                const u32x4 vop = {__builtin_bit_cast(u32x2, x0)[0], __builtin_bit_cast(u32x2, x0)[1],
+                                   __builtin_bit_cast(u32x2, x1)[0], __builtin_bit_cast(u32x2, x1)[1]};
+                oacc[db] = mm::mma(pop[kk], vop, oacc[db]);
+            }
+        }
+    };
+
+    using b0 = std::integral_constant<int, 0>;
+    using b1 = std::integral_constant<int, 1>;
+    const int first = t0 + wave;
+    const int cnt = first < t1 ? (t1 - first + 3) / 4 : 0;
+    auto step = [&](auto buf_tag, int i) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        issue(std::integral_constant<int, 1 - BUF>{}, first + 4 * (i + 1));
+        __builtin_amdgcn_s_waitcnt(fa_vmcnt64(NK + NV));   // tile i's K registers and V tile landed
+        asm volatile("" ::: "memory");
+        compute(buf_tag, first + 4 * i);
+    };
+    if (cnt > 0) {
+        issue(b0{}, first);
+        int i = 0;
+        for (; i + 2 <= cnt; i += 2) {
+            step(b0{}, i);
+            step(b1{}, i + 1);
+        }
+        if (i < cnt) step(b0{}, i);
+        __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
+    }
+
+    // Row statistics of this wave: l summed over the four lane groups (m is already shared).
+    float l_tot = l_run;
+    l_tot += __shfl_xor(l_tot, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+
+    // Combine the four waves in LDS (the V buffers are free once every wave is past its loop).
+    __syncthreads();
+    float* cm = reinterpret_cast<float*>(lds_v);   // [4][16] m, then [4][16] l, then [4][16][D] O
+    float* cl = cm + 4 * DC_ROWS;
+    float* co = cl + 4 * DC_ROWS;
+    if (gq == 0) {
+        cm[wave * DC_ROWS + n] = m_run;
+        cl[wave * DC_ROWS + n] = l_tot;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) co[(wave * DC_ROWS + 4 * gq + e) * D + 16 * db + n] = oacc[db][e];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < rows * D; idx += DC_THREADS) {
+        const int r = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, cm[ww * DC_ROWS + r]);
+        float L = 0.f, O = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) {
+                const float f = exp2f(cm[ww * DC_ROWS + r] - M);
+                L = fmaf(cl[ww * DC_ROWS + r], f, L);
+                O = fmaf(co[(ww * DC_ROWS + r) * D + d], f, O);
+            }
+        }
+        const float o = L > 0.f ? O / L : 0.f;
+        const float lse2 = L > 0.f ? M + log2f(L) : -INFINITY;
+        if (dc.n_split == 1) {
+            uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.q_bs + h * a.q_hs + (int64_t(g.q_start) + r) * a.q_rs;
+            const uint32_t pk = io::pack(o, 0.f);
+            op[d] = uint16_t(pk & 0xffffu);
+            if (d == 0) a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + r] = lse2 * kLn2;
+        } else {
+            const int64_t slot = int64_t(bh) * dc.n_split + split;
+            dc.o_part[(slot * DC_ROWS + r) * D + d] = o;
+            if (d == 0) dc.lse_part[slot * DC_ROWS + r] = lse2;
+        }
+    }
+}
+
+// Combines the splits of fa_decode_split: one workgroup per (batch, head), one thread per
+// column.
+template <typename T>
+__global__ __launch_bounds__(128) void fa_decode_merge(const fa_kargs a, const fa_decode_args dc) {
+    const int bh = blockIdx.x;
+    const int h = bh % a.N, b = bh / a.N;
+    const fa_geom g = fa_geom_of(a, b);
+    const int rows = min(g.sq, DC_ROWS);
+    const int d = threadIdx.x;
+    for (int r = 0; r < rows; ++r) {
+        float M = -INFINITY;
+        for (int sp = 0; sp < dc.n_split; ++sp) M = fmaxf(M, dc.lse_part[(int64_t(bh) * dc.n_split + sp) * DC_ROWS + r]);
+        float L = 0.f, O = 0.f;
+        if (M != -INFINITY) {
+            for (int sp = 0; sp < dc.n_split; ++sp) {
+                const int64_t slot = int64_t(bh) * dc.n_split + sp;
+                const float f = exp2f(dc.lse_part[slot * DC_ROWS + r] - M);
+                L += f;
+                if (d < a.D) O = fmaf(dc.o_part[(slot * DC_ROWS + r) * a.D + d], f, O);
+            }
+        }
+        const int64_t qrow = int64_t(g.q_start) + r;
+        if (d < a.D) {
+            T* op = static_cast<T*>(a.o) + b * a.q_bs + h * a.q_hs + qrow * a.q_rs;
+            op[d] = T(L > 0.f ? O / L : 0.f);
+        }
+        if (d == 0) a.lse[b * a.lse_bs + h * a.lse_hs + qrow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Generic kernel: fp32 arithmetic, any dtype, D <= DMAX.
 // ------------------------------------------------------------------------------------------
 
@@ -1211,7 +1555,7 @@ bool log_enabled() {
 }
 
 fa_status upload_tables(const fa_plan& p, void* workspace, hipStream_t stream) {
-    if (!p.table || p.ws_bytes == 0) return FA_OK;
+    if (!p.table || p.ws_table_bytes == 0) return FA_OK;
     // The image is pageable host memory; hipMemcpyAsync stages it before returning.
     std::vector<unsigned char> image;
     fa_plan_workspace_image(p, &image);
@@ -1254,6 +1598,16 @@ void launch_generic_t(const fa_kargs& a, int D, int alibi, bool dense, dim3 grid
     else fa_fwd_generic<T, 128><<<grid, block, 0, s>>>(a, dense, alibi);
 }
 
+template <int D, bool BF, bool PAGED>
+void launch_decode_d(const fa_kargs& a, const fa_decode_args& dc, int al, dim3 grid, hipStream_t s) {
+    const dim3 block(DC_THREADS);
+    switch (al) {
+        case 0: fa_decode_split<D, BF, 0, PAGED><<<grid, block, 0, s>>>(a, dc); break;
+        case 1: fa_decode_split<D, BF, 1, PAGED><<<grid, block, 0, s>>>(a, dc); break;
+        default: fa_decode_split<D, BF, 2, PAGED><<<grid, block, 0, s>>>(a, dc); break;
+    }
+}
+
 template <int D, bool BF>
 void launch_pp_paged_d(const fa_kargs& a, int al, dim3 grid, hipStream_t s) {
     const dim3 block(PP_THREADS);
@@ -1281,14 +1635,16 @@ fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v,
         if (workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
     }
     if (p.empty) return FA_OK;
-    const int64_t nblocks = p.n_items * p.N;
+    const int64_t nblocks = p.n_items * p.N * p.n_split;
     if (nblocks >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (log_enabled()) {
         std::fprintf(stderr,
                      "[fa] kernel=%s bm=%d bn=%d items/head=%lld blocks=%lld kv tiles visited/full/"
                      "dense=%lld/%lld/%lld table=%d reverse=%d xcd_major=%d ws=%zu paged=%d\n",
-                     p.kernel == FA_KERNEL_PP ? "pingpong" : (p.kernel == FA_KERNEL_MFMA32 ? "mfma32" : "generic"),
+                     p.kernel == FA_KERNEL_PP ? "pingpong"
+                     : p.kernel == FA_KERNEL_MFMA32 ? "mfma32"
+                     : p.kernel == FA_KERNEL_DECODE ? "decode" : "generic",
                      p.bm, p.bn,
                      (long long)p.n_items, (long long)nblocks, (long long)p.kv_tiles_visited,
                      (long long)p.kv_tiles_full, (long long)p.kv_tiles_total, int(p.table),
@@ -1304,7 +1660,37 @@ fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v,
     const bool dense = c.sparse_mode == 1;
     const int32_t dtype = c.dims->dtype;
     (void)hipGetLastError();
-    if (p.kernel == FA_KERNEL_PP && p.paged) {
+    if (p.kernel == FA_KERNEL_DECODE) {
+        fa_decode_args dc{};
+        dc.n_split = p.n_split;
+        if (p.n_split > 1) {
+            dc.o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_opart_offset);
+            dc.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_lse_offset);
+        }
+        const bool bf = dtype == FA_DTYPE_BF16;
+        if (p.D == 128) {
+            if (p.paged) {
+                if (bf) launch_decode_d<128, true, true>(a, dc, alibi, grid, s);
+                else launch_decode_d<128, false, true>(a, dc, alibi, grid, s);
+            } else {
+                if (bf) launch_decode_d<128, true, false>(a, dc, alibi, grid, s);
+                else launch_decode_d<128, false, false>(a, dc, alibi, grid, s);
+            }
+        } else {
+            if (p.paged) {
+                if (bf) launch_decode_d<64, true, true>(a, dc, alibi, grid, s);
+                else launch_decode_d<64, false, true>(a, dc, alibi, grid, s);
+            } else {
+                if (bf) launch_decode_d<64, true, false>(a, dc, alibi, grid, s);
+                else launch_decode_d<64, false, false>(a, dc, alibi, grid, s);
+            }
+        }
+        if (p.n_split > 1) {
+            const dim3 mgrid(static_cast<unsigned>(p.n_items * p.N)), mblock(128);
+            if (bf) fa_decode_merge<__bf16><<<mgrid, mblock, 0, s>>>(a, dc);
+            else fa_decode_merge<_Float16><<<mgrid, mblock, 0, s>>>(a, dc);
+        }
+    } else if (p.kernel == FA_KERNEL_PP && p.paged) {
         const bool bf = dtype == FA_DTYPE_BF16;
         if (p.D == 128) {
             if (bf) launch_pp_paged_d<128, true>(a, alibi, grid, s);

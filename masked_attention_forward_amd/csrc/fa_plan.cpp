@@ -40,6 +40,12 @@ bool prefer_mfma32() {
     return e && std::strcmp(e, "mfma32") == 0;
 }
 
+// FA_DECODE=0 keeps short-query problems on the prefill kernels (for comparisons).
+bool decode_enabled() {
+    const char* e = std::getenv("FA_DECODE");
+    return !(e && e[0] == '0');
+}
+
 }  // namespace
 
 static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool sizes_only,
@@ -171,7 +177,20 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     p.kernel = FA_KERNEL_GENERIC;
     p.bm = FA_GEN_BM;
     p.bn = FA_GEN_BN;
+    // Paged K / V through the MFMA kernels: 64-key tiles inside one page, page offsets in
+    // 32 bits, at most FA_PP_MAX_PAGES pages per sequence.
+    bool paged_mfma_ok = true;
     if (pk) {
+        const int64_t bs = pk->block_size;
+        paged_mfma_ok = (bs & (bs - 1)) == 0 && bs >= FA_PP_BN && ceil_div(max_skv, bs) <= FA_PP_MAX_PAGES &&
+                        bs * d.N * d.D * 2 < (int64_t(1) << 32);
+    }
+    if (mfma_eligible(d.dtype, d.N, d.D) && max_sq <= FA_DEC_ROWS && mode != 1 && paged_mfma_ok &&
+        decode_enabled() && B > 0) {
+        p.kernel = FA_KERNEL_DECODE;
+        p.bm = FA_DEC_ROWS;
+        p.bn = FA_DEC_BN;
+    } else if (pk) {
         // Paged K / V: the ping-pong kernel when its tiles fit whole pages, a sequence has at
         // most FA_PP_MAX_PAGES pages and a page is under 4 GiB; else the generic kernel (any
         // block size, explicit masks too).
@@ -298,7 +317,28 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         }
         return r.end - r.begin;
     };
-    if (p.table) {
+    if (p.kernel == FA_KERNEL_DECODE) {
+        // One work item per batch (all of its <= 16 rows); the kv range is split so that the
+        // launch has about FA_DEC_TARGET_WGS workgroups.
+        p.n_items = B;
+        const int64_t pairs = std::max<int64_t>(B * d.N, 1);
+        const int64_t max_tiles = ceil_div(max_skv, FA_DEC_BN);
+        const int64_t by_wgs = ceil_div(FA_DEC_TARGET_WGS, pairs);
+        const int64_t by_len = std::max<int64_t>(1, max_tiles / FA_DEC_MIN_TILES);
+        p.n_split = int32_t(std::max<int64_t>(1, std::min(by_wgs, by_len)));
+        size_t off = 0;
+        if (p.table) off = align256(size_t(B) * sizeof(fa_geom));
+        p.ws_items_offset = off;
+        if (p.n_split > 1) {
+            const size_t slots = size_t(B) * size_t(d.N) * size_t(p.n_split) * FA_DEC_ROWS;
+            p.ws_opart_offset = off;
+            off = align256(off + slots * size_t(d.D) * sizeof(float));
+            p.ws_lse_offset = off;
+            off = align256(off + slots * sizeof(float));
+        }
+        p.ws_bytes = p.empty ? 0 : off;
+        p.ws_table_bytes = p.table && !p.empty ? p.ws_items_offset : 0;
+    } else if (p.table) {
         p.n_items = p.n_qtiles_total;
         if (with_tables && !sizes_only) {
             std::vector<std::pair<int64_t, int64_t>> order;  // (cost, index)
@@ -325,6 +365,7 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         }
         p.ws_items_offset = align256(size_t(B) * sizeof(fa_geom));
         p.ws_bytes = p.empty ? 0 : p.ws_items_offset + size_t(p.n_items) * 2 * sizeof(int32_t);
+        p.ws_table_bytes = p.ws_bytes;
     } else {
         p.n_qtiles_fixed = int32_t(ceil_div(d.Sq, p.bm));
         p.n_items = B * p.n_qtiles_fixed;
@@ -359,11 +400,12 @@ fa_status fa_make_plan_sizes(const fa_call& call, fa_plan* plan) {
 }
 
 void fa_plan_workspace_image(const fa_plan& plan, std::vector<unsigned char>* image) {
-    image->assign(plan.ws_bytes, 0);
-    if (plan.ws_bytes == 0) return;
+    image->assign(plan.ws_table_bytes, 0);
+    if (plan.ws_table_bytes == 0) return;
     std::memcpy(image->data(), plan.geoms.data(), plan.geoms.size() * sizeof(fa_geom));
-    std::memcpy(image->data() + plan.ws_items_offset, plan.items.data(),
-                plan.items.size() * sizeof(int32_t));
+    if (!plan.items.empty())
+        std::memcpy(image->data() + plan.ws_items_offset, plan.items.data(),
+                    plan.items.size() * sizeof(int32_t));
 }
 
 // ---------------------------------------------------------------------------------------

@@ -31,13 +31,20 @@ struct fa_call {
 };
 
 // Kernel families and their tiles.
-enum { FA_KERNEL_GENERIC = 0, FA_KERNEL_PP = 1, FA_KERNEL_MFMA32 = 2 };
+enum { FA_KERNEL_GENERIC = 0, FA_KERNEL_PP = 1, FA_KERNEL_MFMA32 = 2, FA_KERNEL_DECODE = 3 };
 constexpr int FA_PP_BM = 256;       // 8 waves x 32 rows, two groups in ping-pong
 constexpr int FA_PP_BN = 64;
 constexpr int FA_MFMA32_BM = 128;   // 4 waves x 32 rows
 constexpr int FA_MFMA32_BN = 64;
 constexpr int FA_GEN_BM = 64;
 constexpr int FA_GEN_BN = 16;
+// Split-KV decode (every sequence has at most FA_DEC_ROWS query rows): one workgroup per
+// (batch, head, split), 64-key tiles; splits are sized so the launch has about
+// FA_DEC_TARGET_WGS workgroups and every split at least FA_DEC_MIN_TILES tiles.
+constexpr int FA_DEC_ROWS = 16;
+constexpr int FA_DEC_BN = 64;
+constexpr int FA_DEC_TARGET_WGS = 1024;
+constexpr int FA_DEC_MIN_TILES = 8;
 // Paged K / V in the ping-pong kernel: pages of a power-of-two size >= 64 (a 64-key tile never
 // straddles two pages) and at most this many pages per sequence.
 constexpr int FA_PP_MAX_PAGES = 2048;
@@ -61,7 +68,11 @@ struct fa_plan {
     int64_t n_qtiles_total = 0; // batch-major q tiles over all batches
     int64_t n_kvtiles_max = 0;
     size_t ws_bytes = 0;
+    size_t ws_table_bytes = 0;  // leading part of the workspace the host uploads (geometry, items)
     size_t ws_items_offset = 0;
+    // Split-KV decode: splits per (batch, head) and the partial (O, LSE) buffers in the workspace.
+    int32_t n_split = 1;
+    size_t ws_opart_offset = 0, ws_lse_offset = 0;
     // Strides in elements.
     int64_t q_bs = 0, q_hs = 0, q_rs = 0;
     int64_t kv_bs = 0, kv_hs = 0, kv_rs = 0;
@@ -86,7 +97,8 @@ fa_status fa_make_plan(const fa_call& call, bool with_tables, fa_plan* plan);
 // mode-specific arguments (pre/next, prefix, mask), and builds no work-item list.
 fa_status fa_make_plan_sizes(const fa_call& call, fa_plan* plan);
 
-// Serialises the per-batch geometry and work items into a host image of the workspace.
+// Serialises the per-batch geometry and work items into a host image of the leading
+// ws_table_bytes of the workspace.
 void fa_plan_workspace_image(const fa_plan& plan, std::vector<unsigned char>* image);
 
 #endif  // FA_PLAN_H_

@@ -152,4 +152,12 @@ def workloads() -> dict:
                                         4096, 4096, sparse_mode=5,
                                         prefix=lengths_uniform(4, 0, 4096, seed=55),
                                         alibi=True, seed=55)
+    # Decode shapes (split-KV path): one query row per sequence against a long K/V, a
+    # speculative-decode block of 8 rows, and a varlen decode batch of 32 sequences.
+    w["decode_32k"] = Workload("decode_32k", "BNSD", "bf16", 4, 32, 128, 1, 32768, sparse_mode=3, seed=60)
+    w["decode_spec8_8k"] = Workload("decode_spec8_8k", "BSND", "bf16", 8, 32, 128, 8, 8192, sparse_mode=3,
+                                    seed=61)
+    kvl = lengths_uniform(32, 256, 8192, seed=62)
+    w["decode_varlen"] = Workload("decode_varlen", "TND", "bf16", 32, 32, 128, qlens=[1] * 32, kvlens=kvl,
+                                  sparse_mode=3, seed=62)
     return w

@@ -399,3 +399,37 @@ def test_fwd_paged_workspace_follows_page_size(lib):
     st = lib.fa_fwd_paged(p, p, p, p, p, ctypes.byref(dt), 2, 3, 0, 0, fb._i64(qc), fb._i64(kc), None, None, 0,
                           None, None, ctypes.byref(small), 0.125, p, w16 - 1, None)
     assert st == WORKSPACE
+
+
+# ---------------------------------------------------------------------------------------
+# Split-KV decode planning (host only)
+# ---------------------------------------------------------------------------------------
+
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_decode_plan_split_counts(lib):
+    """At most 16 query rows per sequence selects the split-KV decode kernel (kernel 3, tiles
+    of 16 rows x 64 keys). Splits per (batch, head): enough for ~1024 workgroups, at most one
+    per 8 kv tiles; with more than one split the workspace holds the fp32 partial O
+    [B N splits, 16, D] and LSE [B N splits, 16], 256-byte aligned."""
+    for B, N, skv, n_split in [(1, 1, 333, 1), (1, 2, 5000, 9), (2, 32, 8192, 16), (4, 32, 32768, 8),
+                               (64, 32, 32768, 1)]:
+        d = fb.make_dims(2, 0, B=B, N=N, Sq=1, Skv=skv, D=128)
+        st = fb.fa_plan_stats(d, "BNSD", 3)
+        assert (st["kernel"], st["block_m"], st["block_n"]) == (3, 16, 64)
+        ws = fb.fa_fwd_workspace_size(d, "BNSD", 3)
+        slots = B * N * n_split * 16
+        assert ws == (0 if n_split == 1 else _align256(slots * 128 * 4) + _align256(slots * 4)), (B, N, skv)
+    # 17 rows, an explicit mask, fp32 or D = 96 stay on the other kernels
+    assert fb.fa_plan_stats(fb.make_dims(2, 0, B=1, N=1, Sq=17, Skv=64, D=128), "BNSD", 3)["kernel"] == 1
+    assert fb.fa_plan_stats(fb.make_dims(0, 0, B=1, N=1, Sq=1, Skv=64, D=32), "BNSD", 3)["kernel"] == 0
+    assert fb.fa_plan_stats(fb.make_dims(2, 0, B=1, N=1, Sq=1, Skv=64, D=96), "BNSD", 3)["kernel"] == 0
+    assert fb.fa_plan_stats(fb.make_dims(2, 0, B=1, N=1, Sq=1, Skv=64, D=128), "BNSD", 1,
+                            has_mask=True)["kernel"] == 1
+    # TND: the per-batch geometry table comes first
+    d = tnd([1, 0, 16], [9000, 5, 0])
+    ws = fb.fa_fwd_workspace_size(d, "TND", 3, [1, 1, 17], [9000, 9005, 9005])
+    n_split = max(1, min(-(-1024 // (3 * 2)), -(-9000 // 64) // 8))
+    assert ws == _align256(3 * 32) + _align256(3 * 2 * n_split * 16 * 128 * 4) + _align256(3 * 2 * n_split * 16 * 4)

@@ -281,7 +281,7 @@ def test_parity_alibi_variants(gpu_device, alibi_mode):
 def test_parity_mfma32_kernel(gpu_device, alibi_mode, monkeypatch):
     """The 4-wave MFMA kernel (FA_KERNEL=mfma32, kept for comparisons) against the oracle."""
     monkeypatch.setenv("FA_KERNEL", "mfma32")
-    dims = fb.make_dims(torch.bfloat16, 0, B=1, N=1, Sq=8, Skv=8, D=128)
+    dims = fb.make_dims(torch.bfloat16, 0, B=1, N=1, Sq=64, Skv=64, D=128)   # > 16 rows: not decode
     assert fb.fa_tile_shape(dims, "BNSD")[:2] == (128, 64)
     slopes = ALIBI_SLOPES if alibi_mode else None
     for dtype, D, layout in [("bf16", 128, "BNSD"), ("f16", 64, "BSND")]:
