@@ -34,6 +34,7 @@ KERNEL_SOURCES = ["masked_attention_forward_amd/csrc/fa_kernels.hip",
                   "masked_attention_forward_amd/csrc/fa_plan.cpp",
                   "masked_attention_forward_amd/csrc/fa_plan.h"]
 DOMINANT_KERNEL = "fa_fwd_pp"
+DECODE_KERNEL = "fa_decode_split"
 METRIC = "effective TFLOP/s (unmasked FLOPs) attn fwd bf16 D=128; % of MFMA peak"
 DECODE_METRIC = "effective HBM GB/s attn decode (Q, K, V read once, O and LSE written once)"
 
@@ -55,10 +56,10 @@ def kernel_sources_sha(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, path=None, sources=None):
+def recorded_traffic(workload: str, path=None, sources=None, kernel=DOMINANT_KERNEL):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel sources; else None."""
-    path = path or os.path.join(ROOT, "profiles", f"{DOMINANT_KERNEL}_{workload}_counters.md")
+    path = path or os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -310,9 +311,10 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = recorded_traffic(args.workload) if paged is None else None
     # At most 16 query rows per sequence: the split-KV decode path, bound by HBM.
     decode = max(w.qlens) <= 16 if w.layout == "TND" else w.Sq <= 16
+    traffic = (recorded_traffic(args.workload, kernel=DECODE_KERNEL if decode else DOMINANT_KERNEL)
+               if paged is None else None)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
 
     res = {
