@@ -17,3 +17,4 @@ from .attention import (  # noqa: F401
     visible,
     visible_matrix,
 )
+from .backward import attention_backward, attention_head_backward  # noqa: F401
