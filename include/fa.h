@@ -128,6 +128,34 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  const uint8_t* atten_mask, const int64_t* mask_bcast,
                  float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass: gradients of a loss with respect to q, k and v, given dout = dLoss/dO. No
+ * page gives a backward pass; this is the derivative of the forward defined above. With P
+ * recomputed from q, k, the bias and the mask, and the forward's softmax_lse:
+ *   P_ij = exp(scale q_i.k_j + bias_ij - LSE_i) for visible (i, j), else 0;
+ *   Delta_i = sum_d dout_id out_id;
+ *   dV = P^T dout,  dP = dout V^T,  dS = P * (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, k, v:          the forward's inputs; out, softmax_lse: what fa_fwd returned for them.
+ *   dout:             device, dims->dtype, out's layout.
+ *   dq, dk, dv:       device, dims->dtype, the layouts of q, k and v; every element is written
+ *                     (zero where no visible pair contributes).
+ *   workspace:        at least fa_bwd_workspace_size bytes (Delta, and the per-batch geometry in
+ *                     TND / prefix modes).
+ * Every other argument, its validation and the status codes are fa_fwd's. Gradients accumulate
+ * in fp32; with fp16 / bf16 inputs P and dS are rounded to that type for the products that
+ * consume them. No atomics: results are bitwise deterministic. */
+fa_status fa_bwd_workspace_size(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                                const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                                size_t* bytes);
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out,
+                 const float* softmax_lse, const void* dout, void* dq, void* dk, void* dv,
+                 const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                 int64_t pre_tokens, int64_t next_tokens,
+                 const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                 const int64_t* prefix, const float* alibi_slopes, int32_t alibi_mode,
+                 const uint8_t* atten_mask, const int64_t* mask_bcast,
+                 float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Mask probe: runs the same device mask code the forward kernels use, without any
  * attention arithmetic.
  *   row_visible_counts: device int64, laid out like softmax_lse ([B, N, Sq] or [N, T_q]):

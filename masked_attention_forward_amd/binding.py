@@ -98,6 +98,11 @@ def load_library():
     lib.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
                                  vp, i32, vp, pi64, ppaged, ctypes.c_float, vp, sz, vp]
     lib.fa_fwd_paged.restype = i32
+    lib.fa_bwd_workspace_size.argtypes = [pdims, i32, i32, pi64, pi64, ctypes.POINTER(sz)]
+    lib.fa_bwd_workspace_size.restype = i32
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
+                           vp, i32, vp, pi64, ctypes.c_float, vp, sz, vp]
+    lib.fa_bwd.restype = i32
     _LIB = lib
     return lib
 
@@ -348,6 +353,58 @@ def paged_attention(q, key_cache, value_cache, block_table, *, layout="BNSD", ca
     fa_fwd_paged(q, key_cache, value_cache, block_table, out, lse, layout=layout, cache_layout=cache_layout,
                  kv_seqlen=kv_seqlen, sparse_mode=sparse_mode, scale=scale, workspace=workspace, **kw)
     return out, lse
+
+
+def fa_bwd_workspace_size(dims: FaDims, layout, sparse_mode: int, actual_seq_qlen=None,
+                          actual_seq_kvlen=None) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    st = lib.fa_bwd_workspace_size(ctypes.byref(dims), _layout_code(layout), int(sparse_mode),
+                                   _i64(actual_seq_qlen), _i64(actual_seq_kvlen), ctypes.byref(out))
+    if st != 0:
+        raise FaError(st, "fa_bwd_workspace_size")
+    return int(out.value)
+
+
+def fa_bwd(q, k, v, out, softmax_lse, dout, dq, dk, dv, *, layout="BNSD", sparse_mode: int = 0,
+           pre_tokens: int = 0, next_tokens: int = 0, actual_seq_qlen=None, actual_seq_kvlen=None, prefix=None,
+           alibi_slopes: Optional[torch.Tensor] = None, alibi_mode="right",
+           atten_mask: Optional[torch.Tensor] = None, mask_bcast=None, scale: float,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Calls fa_bwd: dq, dk, dv (written in full) from the forward's inputs, its out and
+    softmax_lse, and dout. Raises FaError on a non-zero status."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_device_tensor(name, t, q.dtype)
+    _check_device_tensor("softmax_lse", softmax_lse, torch.float32)
+    _check_device_tensor("alibi_slopes", alibi_slopes, torch.float32)
+    if atten_mask is not None:
+        _check_device_tensor("atten_mask", atten_mask)
+        if atten_mask.dtype not in (torch.uint8, torch.bool):
+            raise TypeError("atten_mask must be uint8 or bool")
+    for name, t, ref in (("out", out, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have shape {tuple(ref.shape)}, got {tuple(t.shape)}")
+    dims = dims_of(q, k, layout, actual_seq_qlen)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                    ctypes.byref(dims), _layout_code(layout), int(sparse_mode), int(pre_tokens), int(next_tokens),
+                    _i64(actual_seq_qlen), _i64(actual_seq_kvlen), _i64(prefix), _ptr(alibi_slopes),
+                    _alibi_code(alibi_mode), _ptr(atten_mask), _i64(mask_bcast), float(scale), _ptr(workspace), ws_bytes,
+                    stream if stream is not None else _stream(q.device))
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+
+
+def flash_attention_backward(q, k, v, out, lse, dout, *, layout="BNSD", sparse_mode: int = 0, scale: float, **kw):
+    """Allocates dq / dk / dv / workspace and runs fa_bwd. Returns (dq, dk, dv)."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dims = dims_of(q, k, layout, kw.get("actual_seq_qlen"))
+    ws = fa_bwd_workspace_size(dims, layout, sparse_mode, kw.get("actual_seq_qlen"), kw.get("actual_seq_kvlen"))
+    workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    fa_bwd(q, k, v, out, lse, dout, dq, dk, dv, layout=layout, sparse_mode=sparse_mode, scale=scale,
+           workspace=workspace, **kw)
+    return dq, dk, dv
 
 
 def lse_shape(q, layout, actual_seq_qlen=None):

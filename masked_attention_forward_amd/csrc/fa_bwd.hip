@@ -1,0 +1,821 @@
+// fa_bwd.hip - backward pass of masked attention for gfx950 (dQ, dK, dV) and its C ABI.
+//
+// The pages define the forward only; the backward is its derivative. With P recomputed from
+// Q, K, the bias and the mask of the forward ("sparseMode介绍" sparseMode 0..8, "压缩mask"
+// alibi) and the forward's LSE:
+//
+//     P_ij = exp(scale q_i.k_j + bias_ij - LSE_i) for visible (i, j), else 0
+//     Delta_i = sum_d dO_id O_id                  (= sum_j P_ij dP_ij)
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - Delta),   dQ = scale dS K,   dK = scale dS^T Q
+//
+// Three kernels run in order: fa_bwd_delta (Delta from O and dO), one that owns a block of keys
+// and loops over the query tiles that see it (dK, dV), and one that owns a block of query rows
+// and loops over the kv tiles it sees (dQ). Every output element is written by exactly one
+// workgroup: no atomics, bitwise deterministic.
+//
+//  * MFMA kernels (fp16 / bf16, D in {64, 128}, every mode but the explicit mask): four waves
+//    own 16 keys (dK dV) or 16 query rows (dQ) each, with 16x16x32 MFMAs. The products whose
+//    contraction runs over rows or keys take their left operand straight from the accumulators
+//    of the preceding product: tile rows are permuted so that a lane's four values of one
+//    16 x 16 block and of its neighbour are the eight consecutive rows (keys) the next MFMA
+//    wants (block b, row r holds 32 (b / 2) + 8 (r / 4) + 4 (b % 2) + r % 4). Their right
+//    operand (8 consecutive rows of one column) comes from LDS through ds_read_b64_tr_b16.
+//  * Generic kernels: any dtype, D <= 128, the explicit mask: one thread per query row (dQ) or
+//    per key (dK, dV), fp32 throughout.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <vector>
+
+#include "fa_device.h"
+#include "fa_mask.h"
+#include "fa_plan.h"
+
+namespace {
+
+struct fa_bwd_args {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    const float* lse;
+    float* delta;            // laid out like lse (workspace)
+    const float* slopes;
+    const uint8_t* mask;
+    const fa_geom* geoms;    // per-batch table (workspace) or nullptr
+    fa_geom geom0;
+    int64_t q_bs, q_hs, q_rs;
+    int64_t kv_bs, kv_hs, kv_rs;
+    int64_t lse_bs, lse_hs;
+    int64_t m_bs, m_hs, m_rs;
+    int32_t B, N, D;
+    int32_t n_qt, n_kt;      // 64-row q tiles / 64-key kv tiles of the longest sequence
+    int32_t alibi_left;
+    float scale_log2;        // scale * log2(e)
+    float scale;
+};
+
+constexpr int BW_THREADS = 256;
+constexpr int BW_T = 64;        // rows per q tile, keys per kv tile
+constexpr int GB_ROWS = 64;     // generic kernels: threads (rows or keys) per workgroup
+constexpr int GB_T = 16;        // generic kernels: staged rows / keys per step
+
+__device__ __forceinline__ fa_geom bw_geom(const fa_bwd_args& a, int b) {
+    if (!a.geoms) return a.geom0;
+    const fa_geom t = a.geoms[b];
+    fa_geom g;
+    g.q_start = fa_uniform(t.q_start);
+    g.kv_start = fa_uniform(t.kv_start);
+    g.sq = fa_uniform(t.sq);
+    g.skv = fa_uniform(t.skv);
+    g.a = fa_uniform(t.a);
+    g.c = fa_uniform(t.c);
+    g.f = fa_uniform(t.f);
+    g.pad = 0;
+    return g;
+}
+
+// Query rows [lo, hi] (batch-local) that can see a key in [j0, j1]: lo(i) <= j1 and hi(i) >= j0,
+// a superset of the rows with a visible key there (masking removes the rest).
+__device__ __forceinline__ void bw_row_range(const fa_geom& g, int j0, int j1, int& lo, int& hi) {
+    lo = g.f >= j0 ? 0 : max(0, j0 - g.c);
+    hi = min(g.sq - 1, j1 - g.a);
+}
+
+// Alibi bias in the log2 domain (AL: 1 linear, right- or left-aligned per aoff; 2 square root).
+template <int AL>
+__device__ __forceinline__ float bw_bias2(float slope2, int i, int j, int off, int aoff) {
+    if (AL == 1) return slope2 * float(j - i - aoff);
+    if (AL == 2) {
+        const float dd = float(i + off - j);
+        return -slope2 * copysignf(__builtin_amdgcn_sqrtf(fabsf(dd)), dd);
+    }
+    return 0.f;
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f(T x) {
+    return float(x);
+}
+
+// ------------------------------------------------------------------------------------------
+// Delta_i = sum_d dO_id O_id (fp32), one wave per query row.
+// ------------------------------------------------------------------------------------------
+constexpr int DL_ROWS = BW_THREADS / 64;   // rows per workgroup of fa_bwd_delta
+
+template <typename T>
+__global__ __launch_bounds__(BW_THREADS) void fa_bwd_delta(const fa_bwd_args a) {
+    const int nrb = (a.n_qt * BW_T + DL_ROWS - 1) / DL_ROWS;
+    const int bh = blockIdx.x / nrb;
+    const int b = bh / a.N, h = bh % a.N;
+    const fa_geom g = bw_geom(a, b);
+    const int i = (blockIdx.x % nrb) * DL_ROWS + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (i >= g.sq) return;
+    const int64_t ro = b * a.q_bs + h * a.q_hs + (int64_t(g.q_start) + i) * a.q_rs;
+    const T* op = static_cast<const T*>(a.o) + ro;
+    const T* dp = static_cast<const T*>(a.dout) + ro;
+    float s = 0.f;
+    for (int d = lane; d < a.D; d += 64) s = fmaf(to_f(op[d]), to_f(dp[d]), s);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if (lane == 0) a.delta[b * a.lse_bs + h * a.lse_hs + g.q_start + i] = s;
+}
+
+// ------------------------------------------------------------------------------------------
+// Generic kernels (fp32 arithmetic).
+// ------------------------------------------------------------------------------------------
+template <bool DENSE>
+__device__ __forceinline__ bool bw_visible(const fa_bwd_args& a, const fa_geom& g, int b, int h, int i, int j) {
+    if (i < 0 || i >= g.sq || j < 0 || j >= g.skv) return false;
+    if (DENSE) return a.mask[b * a.m_bs + h * a.m_hs + int64_t(i) * a.m_rs + j] == 0;
+    return j >= fa_row_lo(g, i) && j <= fa_row_hi(g, i);
+}
+
+// dQ: one thread per query row; K / V tiles of GB_T keys staged in LDS.
+template <typename T, int DMAX, bool DENSE, int AL>
+__global__ __launch_bounds__(GB_ROWS) void fa_bwd_dq_generic(const fa_bwd_args a) {
+    __shared__ float qs[GB_ROWS][DMAX + 1], dos[GB_ROWS][DMAX + 1];
+    __shared__ float ks[GB_T][DMAX], vs[GB_T][DMAX];
+    const int nqt = (a.n_qt * BW_T + GB_ROWS - 1) / GB_ROWS;
+    const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
+    const int b = bh / a.N, h = bh % a.N;
+    const fa_geom g = bw_geom(a, b);
+    const int i0 = qt * GB_ROWS;
+    if (i0 >= g.sq) return;
+    const int D = a.D, tid = threadIdx.x, i = i0 + tid;
+    const T* qp = static_cast<const T*>(a.q) + b * a.q_bs + h * a.q_hs + int64_t(g.q_start) * a.q_rs;
+    const T* dop = static_cast<const T*>(a.dout) + b * a.q_bs + h * a.q_hs + int64_t(g.q_start) * a.q_rs;
+    const T* kp = static_cast<const T*>(a.k) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+    const T* vp = static_cast<const T*>(a.v) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+    for (int e = tid; e < GB_ROWS * DMAX; e += GB_ROWS) {
+        const int r = e / DMAX, d = e % DMAX;
+        const bool ok = i0 + r < g.sq && d < D;
+        qs[r][d] = ok ? to_f(qp[int64_t(i0 + r) * a.q_rs + d]) : 0.f;
+        dos[r][d] = ok ? to_f(dop[int64_t(i0 + r) * a.q_rs + d]) : 0.f;
+    }
+    const bool row_ok = i < g.sq;
+    const int64_t li = b * a.lse_bs + h * a.lse_hs + g.q_start + (row_ok ? i : 0);
+    const float lse2 = row_ok ? a.lse[li] * kLog2e : 0.f;
+    const float dlt = row_ok ? a.delta[li] : 0.f;
+    const float slope2 = AL ? a.slopes[h] * kLog2e : 0.f;
+    const int off = g.skv - g.sq, aoff = a.alibi_left ? 0 : off;
+    float dq[DMAX];
+#pragma unroll
+    for (int d = 0; d < DMAX; ++d) dq[d] = 0.f;
+    const int i1 = min(i0 + GB_ROWS, g.sq) - 1;
+    const fa_kv_range kr = DENSE ? fa_kv_range{0, (g.skv + GB_T - 1) / GB_T} : fa_tile_kv_range(g, i0, i1, GB_T);
+    for (int kt = kr.begin; kt < kr.end; ++kt) {
+        const int j0 = kt * GB_T;
+        __syncthreads();
+        for (int e = tid; e < GB_T * DMAX; e += GB_ROWS) {
+            const int r = e / DMAX, d = e % DMAX;
+            const bool ok = j0 + r < g.skv && d < D;
+            ks[r][d] = ok ? to_f(kp[int64_t(j0 + r) * a.kv_rs + d]) : 0.f;
+            vs[r][d] = ok ? to_f(vp[int64_t(j0 + r) * a.kv_rs + d]) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int jj = 0; jj < GB_T; ++jj) {
+            const int j = j0 + jj;
+            if (!bw_visible<DENSE>(a, g, b, h, i, j)) continue;
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int d = 0; d < DMAX; ++d) {
+                s = fmaf(qs[tid][d], ks[jj][d], s);
+                dp = fmaf(dos[tid][d], vs[jj][d], dp);
+            }
+            const float p = exp2f(fmaf(s, a.scale_log2, bw_bias2<AL>(slope2, i, j, off, aoff)) - lse2);
+            const float ds = p * (dp - dlt);
+#pragma unroll
+            for (int d = 0; d < DMAX; ++d) dq[d] = fmaf(ds, ks[jj][d], dq[d]);
+        }
+    }
+    if (row_ok) {
+        T* out = static_cast<T*>(a.dq) + b * a.q_bs + h * a.q_hs + (int64_t(g.q_start) + i) * a.q_rs;
+#pragma unroll
+        for (int d = 0; d < DMAX; ++d)
+            if (d < D) out[d] = T(dq[d] * a.scale);
+    }
+}
+
+// dK (WHICH = 1) or dV (WHICH = 0): one thread per key; Q / dO tiles of GB_T rows in LDS.
+template <typename T, int DMAX, bool DENSE, int AL, int WHICH>
+__global__ __launch_bounds__(GB_ROWS) void fa_bwd_dkdv_generic(const fa_bwd_args a) {
+    __shared__ float ks[GB_ROWS][DMAX + 1], vs[GB_ROWS][DMAX + 1];
+    __shared__ float qs[GB_T][DMAX], dos[GB_T][DMAX];
+    __shared__ float ls[GB_T], dls[GB_T];
+    const int nkt = (a.n_kt * BW_T + GB_ROWS - 1) / GB_ROWS;
+    const int bh = blockIdx.x / nkt, kt = blockIdx.x % nkt;
+    const int b = bh / a.N, h = bh % a.N;
+    const fa_geom g = bw_geom(a, b);
+    const int j0 = kt * GB_ROWS;
+    if (j0 >= g.skv) return;
+    const int D = a.D, tid = threadIdx.x, j = j0 + tid;
+    const T* qp = static_cast<const T*>(a.q) + b * a.q_bs + h * a.q_hs + int64_t(g.q_start) * a.q_rs;
+    const T* dop = static_cast<const T*>(a.dout) + b * a.q_bs + h * a.q_hs + int64_t(g.q_start) * a.q_rs;
+    const T* kp = static_cast<const T*>(a.k) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+    const T* vp = static_cast<const T*>(a.v) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+    for (int e = tid; e < GB_ROWS * DMAX; e += GB_ROWS) {
+        const int r = e / DMAX, d = e % DMAX;
+        const bool ok = j0 + r < g.skv && d < D;
+        ks[r][d] = ok ? to_f(kp[int64_t(j0 + r) * a.kv_rs + d]) : 0.f;
+        vs[r][d] = ok ? to_f(vp[int64_t(j0 + r) * a.kv_rs + d]) : 0.f;
+    }
+    const float slope2 = AL ? a.slopes[h] * kLog2e : 0.f;
+    const int off = g.skv - g.sq, aoff = a.alibi_left ? 0 : off;
+    float acc[DMAX];
+#pragma unroll
+    for (int d = 0; d < DMAX; ++d) acc[d] = 0.f;
+    int r_lo = 0, r_hi = g.sq - 1;
+    if (!DENSE) bw_row_range(g, j0, min(j0 + GB_ROWS, g.skv) - 1, r_lo, r_hi);
+    for (int t0 = (r_lo / GB_T) * GB_T; t0 <= r_hi; t0 += GB_T) {
+        __syncthreads();
+        for (int e = tid; e < GB_T * DMAX; e += GB_ROWS) {
+            const int r = e / DMAX, d = e % DMAX;
+            const bool ok = t0 + r < g.sq && d < D;
+            qs[r][d] = ok ? to_f(qp[int64_t(t0 + r) * a.q_rs + d]) : 0.f;
+            dos[r][d] = ok ? to_f(dop[int64_t(t0 + r) * a.q_rs + d]) : 0.f;
+        }
+        if (tid < GB_T) {
+            const bool ok = t0 + tid < g.sq;
+            const int64_t li = b * a.lse_bs + h * a.lse_hs + g.q_start + (ok ? t0 + tid : 0);
+            ls[tid] = ok ? a.lse[li] * kLog2e : 0.f;
+            dls[tid] = ok ? a.delta[li] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int ii = 0; ii < GB_T; ++ii) {
+            const int i = t0 + ii;
+            if (!bw_visible<DENSE>(a, g, b, h, i, j)) continue;
+            float s = 0.f;
+#pragma unroll
+            for (int d = 0; d < DMAX; ++d) s = fmaf(qs[ii][d], ks[tid][d], s);
+            const float p = exp2f(fmaf(s, a.scale_log2, bw_bias2<AL>(slope2, i, j, off, aoff)) - ls[ii]);
+            if (WHICH == 0) {
+#pragma unroll
+                for (int d = 0; d < DMAX; ++d) acc[d] = fmaf(p, dos[ii][d], acc[d]);
+            } else {
+                float dp = 0.f;
+#pragma unroll
+                for (int d = 0; d < DMAX; ++d) dp = fmaf(dos[ii][d], vs[tid][d], dp);
+                const float ds = p * (dp - dls[ii]);
+#pragma unroll
+                for (int d = 0; d < DMAX; ++d) acc[d] = fmaf(ds, qs[ii][d], acc[d]);
+            }
+        }
+    }
+    if (j < g.skv) {
+        T* out = static_cast<T*>(WHICH == 0 ? a.dv : a.dk) + b * a.kv_bs + h * a.kv_hs +
+                 (int64_t(g.kv_start) + j) * a.kv_rs;
+        const float f = WHICH == 0 ? 1.f : a.scale;
+#pragma unroll
+        for (int d = 0; d < DMAX; ++d)
+            if (d < D) out[d] = T(acc[d] * f);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// MFMA kernels.
+// ------------------------------------------------------------------------------------------
+
+// LDS tiles are 64 rows x D, row-major in 16-byte chunks; chunk c of row r sits at c ^ swz(r).
+// The A-operand reads touch rows 8 (n / 4) + n % 4 (+ const) for n = 0..15 at one chunk: swz
+// maps those 16 rows to distinct values for D = 128 (bits 0-1 and 3-4 of r).
+template <int KCH>
+__device__ __forceinline__ int bw_swz(int r) {
+    if constexpr (KCH == 16) return (r & 3) | (((r >> 3) & 3) << 2);
+    else return (r & 3) | (((r >> 3) & 1) << 2);
+}
+
+// Row (or key) held by value e of a lane in group gq for 16 x 16 block bb of a 64-row tile:
+// 32 (bb / 2) + 8 gq + 4 (bb % 2) + e. The A operand of block bb in row slot n holds
+// perm_row(bb, n) = 32 (bb / 2) + 8 (n / 4) + 4 (bb % 2) + n % 4.
+__device__ __forceinline__ int bw_perm(int bb, int r) { return 32 * (bb >> 1) + 8 * (r >> 2) + 4 * (bb & 1) + (r & 3); }
+
+// Cooperative HBM -> LDS load of a 64-row tile (rows past `rows` read as zeros).
+template <int D>
+__device__ __forceinline__ void bw_tile_load(const uint16_t* base, int rs, int rows, u32x4* dst) {
+    constexpr int KCH = D / 8;
+    constexpr int NLD = BW_T * KCH / BW_THREADS;
+    const __amdgpu_buffer_rsrc_t r = fa_rsrc(base, rows > 0 ? ((rows - 1) * rs + D) * 2 : 0);
+    const int wave = fa_uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+#pragma unroll
+    for (int p = 0; p < NLD; ++p) {
+        const int c = p * BW_THREADS + wave * 64 + lane;
+        const int row = c / KCH, cc = c % KCH;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + p * BW_THREADS + wave * 64), 16,
+                                                 (row * rs + (cc ^ bw_swz<KCH>(row)) * 8) * 2, 0, 0, 0);
+    }
+}
+
+// Two tiles of the same rows (K and V, or Q and dO) starting at row r0.
+template <int D>
+__device__ __forceinline__ void bw_load2(const uint16_t* x, const uint16_t* y, int r0, int rs, int rows, u32x4* dx,
+                                         u32x4* dy) {
+    bw_tile_load<D>(x + int64_t(r0) * rs, rs, rows, dx);
+    bw_tile_load<D>(y + int64_t(r0) * rs, rs, rows, dy);
+}
+
+// A operand (16 B) of row `row`, logical chunk c, from a swizzled LDS tile.
+template <int D>
+__device__ __forceinline__ u32x4 bw_arow(const u32x4* tile, int row, int c) {
+    constexpr int KCH = D / 8;
+    return tile[row * KCH + (c ^ bw_swz<KCH>(row))];
+}
+
+// B operand: rows 32 kk + 8 gq + 0..7 of column 16 db + n, through two transpose reads.
+template <int D>
+__device__ __forceinline__ u32x4 bw_bcol(const u32x4* tile, int kk, int db, int gq, int n) {
+    constexpr int KCH = D / 8;
+    const char* base = reinterpret_cast<const char*>(tile);
+    u32x4 out;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int row = 32 * kk + 8 * gq + 4 * hf + (n >> 2);
+        const int byte = 32 * db + 8 * (n & 3);          // within the logical row
+        const int chunk = (byte >> 4) ^ bw_swz<KCH>(row);
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(base + (row * KCH + chunk) * 16 + (byte & 15)));
+        out[2 * hf] = __builtin_bit_cast(u32x2, x)[0];
+        out[2 * hf + 1] = __builtin_bit_cast(u32x2, x)[1];
+    }
+    return out;
+}
+
+// dQ: four waves x 16 query rows; kv tiles of 64 keys through LDS (double-buffered).
+template <int D, bool IS_BF16, int AL>
+__global__ __launch_bounds__(BW_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args a) {
+    using io = mfma_io<IS_BF16>;
+    using mm = mfma16_io<IS_BF16>;
+    constexpr int KD = D / 32, DB = D / 16, TILE_U4 = BW_T * D / 8;
+    __shared__ u32x4 lds_k[2][TILE_U4], lds_v[2][TILE_U4];
+    const int lane = threadIdx.x & 63, wave = fa_uniform(threadIdx.x >> 6);
+    const int n = lane & 15, gq = lane >> 4;
+    const int bh = blockIdx.x / a.n_qt, qt = blockIdx.x % a.n_qt;
+    const int b = bh / a.N, h = bh % a.N;
+    const fa_geom g = bw_geom(a, b);
+    const int i0 = qt * BW_T;
+    if (i0 >= g.sq) return;
+    const int q_rs = int(a.q_rs), kv_rs = int(a.kv_rs);
+    const int64_t qo = b * a.q_bs + h * a.q_hs + int64_t(g.q_start) * a.q_rs;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qo;
+    const uint16_t* dop = static_cast<const uint16_t*>(a.dout) + qo;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+
+    // This lane's query row (the S^T column) and its operands.
+    const int i = i0 + 16 * wave + n;
+    const bool row_ok = i < g.sq;
+    u32x4 qop[KD], dop_[KD];
+    {
+        const int bytes = ((g.sq - 1) * q_rs + D) * 2;
+        const __amdgpu_buffer_rsrc_t rq = fa_rsrc(qp, bytes), rd = fa_rsrc(dop, bytes);
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd) {
+            qop[kd] = fa_bload(rq, (i * q_rs + 32 * kd + 8 * gq) * 2);
+            dop_[kd] = fa_bload(rd, (i * q_rs + 32 * kd + 8 * gq) * 2);
+        }
+    }
+    const int64_t li = b * a.lse_bs + h * a.lse_hs + g.q_start + (row_ok ? i : 0);
+    const float lse2 = row_ok ? a.lse[li] * kLog2e : INFINITY;
+    const float dlt = row_ok ? a.delta[li] : 0.f;
+    const int row_lo = fa_row_lo(g, i), row_hi = fa_row_hi(g, i);
+    const float sl2 = a.scale_log2;
+    const float slope2 = AL ? a.slopes[h] * kLog2e : 0.f;
+    const int off = g.skv - g.sq, aoff = a.alibi_left ? 0 : off;
+
+    const fa_kv_range kr = fa_tile_kv_range(g, i0, min(i0 + BW_T, g.sq) - 1, BW_T);
+    f32x4 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x4{};
+    // kv tile kt (none past the range: zeros, nothing read) into buffer buf.
+#define BW_LOAD_KV(kt, buf) \
+    bw_load2<D>(kp, vp, (kt) * BW_T, kv_rs, (kt) < kr.end ? min(BW_T, g.skv - (kt) * BW_T) : 0, lds_k[buf], lds_v[buf])
+    if (kr.begin < kr.end) BW_LOAD_KV(kr.begin, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = kr.begin; kt < kr.end; ++kt) {
+        const int buf = (kt - kr.begin) & 1;
+        BW_LOAD_KV(kt + 1, buf ^ 1);
+        const u32x4* kt_ = lds_k[buf];
+        const u32x4* vt_ = lds_v[buf];
+        f32x4 s[4], dp[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            s[bb] = f32x4{};
+            dp[bb] = f32x4{};
+            const int key = bw_perm(bb, n);
+#pragma unroll
+            for (int kd = 0; kd < KD; ++kd) {
+                s[bb] = mm::mma(bw_arow<D>(kt_, key, 4 * kd + gq), qop[kd], s[bb]);
+                dp[bb] = mm::mma(bw_arow<D>(vt_, key, 4 * kd + gq), dop_[kd], dp[bb]);
+            }
+        }
+        const int j0 = kt * BW_T;
+        float ds[16];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 32 * (bb >> 1) + 8 * gq + 4 * (bb & 1) + e;
+                const bool vis = row_ok && j >= row_lo && j <= row_hi;
+                const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[bb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - lse2)
+                                    : 0.f;
+                ds[4 * bb + e] = p * (dp[bb][e] - dlt);
+            }
+        }
+        u32x4 dsop[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const float* lo = ds + 8 * kk;
+            const float* hi = ds + 8 * kk + 4;
+            dsop[kk] = u32x4{io::pack(lo[0], lo[1]), io::pack(lo[2], lo[3]), io::pack(hi[0], hi[1]),
+                             io::pack(hi[2], hi[3])};
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) acc[db] = mm::mma(dsop[kk], bw_bcol<D>(kt_, kk, db, gq, n), acc[db]);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+#undef BW_LOAD_KV
+    // Rows 16 wave + 4 gq + e, columns 16 db + n.
+    uint16_t* out = static_cast<uint16_t*>(a.dq) + qo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = i0 + 16 * wave + 4 * gq + e;
+        if (r < g.sq) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                out[int64_t(r) * q_rs + 16 * db + n] = uint16_t(io::pack(acc[db][e] * a.scale, 0.f) & 0xffffu);
+        }
+    }
+}
+
+// dK and dV: four waves x 16 keys; q tiles of 64 rows (Q, dO, LSE, Delta) through LDS.
+template <int D, bool IS_BF16, int AL>
+__global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args a) {
+    using io = mfma_io<IS_BF16>;
+    using mm = mfma16_io<IS_BF16>;
+    constexpr int KD = D / 32, DB = D / 16, TILE_U4 = BW_T * D / 8;
+    __shared__ u32x4 lds_q[2][TILE_U4], lds_do[2][TILE_U4];
+    __shared__ __attribute__((aligned(16))) float lds_l[2][BW_T];
+    __shared__ __attribute__((aligned(16))) float lds_dl[2][BW_T];
+    const int lane = threadIdx.x & 63, wave = fa_uniform(threadIdx.x >> 6);
+    const int n = lane & 15, gq = lane >> 4;
+    const int bh = blockIdx.x / a.n_kt, kt = blockIdx.x % a.n_kt;
+    const int b = bh / a.N, h = bh % a.N;
+    const fa_geom g = bw_geom(a, b);
+    const int j0 = kt * BW_T;
+    if (j0 >= g.skv) return;
+    const int q_rs = int(a.q_rs), kv_rs = int(a.kv_rs);
+    const int64_t qo = b * a.q_bs + h * a.q_hs + int64_t(g.q_start) * a.q_rs;
+    const int64_t ko = b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qo;
+    const uint16_t* dop = static_cast<const uint16_t*>(a.dout) + qo;
+
+    // This lane's key (the S column) and its operands.
+    const int j = j0 + 16 * wave + n;
+    u32x4 kop[KD], vop[KD];
+    {
+        const int bytes = ((g.skv - 1) * kv_rs + D) * 2;
+        const __amdgpu_buffer_rsrc_t rk = fa_rsrc(static_cast<const uint16_t*>(a.k) + ko, bytes);
+        const __amdgpu_buffer_rsrc_t rv = fa_rsrc(static_cast<const uint16_t*>(a.v) + ko, bytes);
+#pragma unroll
+        for (int kd = 0; kd < KD; ++kd) {
+            kop[kd] = fa_bload(rk, (j * kv_rs + 32 * kd + 8 * gq) * 2);
+            vop[kd] = fa_bload(rv, (j * kv_rs + 32 * kd + 8 * gq) * 2);
+        }
+    }
+    const float sl2 = a.scale_log2;
+    const float slope2 = AL ? a.slopes[h] * kLog2e : 0.f;
+    const int off = g.skv - g.sq, aoff = a.alibi_left ? 0 : off;
+    int r_lo, r_hi;
+    bw_row_range(g, j0, min(j0 + BW_T, g.skv) - 1, r_lo, r_hi);
+    const int t_begin = r_lo / BW_T, t_end = r_lo <= r_hi ? r_hi / BW_T + 1 : t_begin;
+
+    f32x4 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        dk[db] = f32x4{};
+        dv[db] = f32x4{};
+    }
+    const int tid = threadIdx.x;
+    // LSE (log2 domain, +inf past the sequence so that P = 0) and Delta of q tile t.
+    auto stats = [&](int t, float& l2, float& dl) {
+        const int r = t * BW_T + tid;
+        const bool ok = tid < BW_T && t < t_end && r < g.sq;
+        const int64_t li = b * a.lse_bs + h * a.lse_hs + g.q_start + (ok ? r : 0);
+        l2 = ok ? a.lse[li] * kLog2e : INFINITY;
+        dl = ok ? a.delta[li] : 0.f;
+    };
+    // q tile t (none past the range: zeros, nothing read) into buffer buf.
+#define BW_LOAD_Q(t, buf) \
+    bw_load2<D>(qp, dop, (t) * BW_T, q_rs, (t) < t_end ? min(BW_T, g.sq - (t) * BW_T) : 0, lds_q[buf], lds_do[buf])
+    if (t_begin < t_end) {
+        float l2, dl;
+        stats(t_begin, l2, dl);
+        BW_LOAD_Q(t_begin, 0);
+        if (tid < BW_T) {
+            lds_l[0][tid] = l2;
+            lds_dl[0][tid] = dl;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = t_begin; t < t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        float l2n, dln;
+        stats(t + 1, l2n, dln);
+        BW_LOAD_Q(t + 1, buf ^ 1);
+        const u32x4* qt_ = lds_q[buf];
+        const u32x4* dt_ = lds_do[buf];
+        const int i0 = t * BW_T;
+        f32x4 s[4], dp[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            s[rb] = f32x4{};
+            dp[rb] = f32x4{};
+            const int row = bw_perm(rb, n);
+#pragma unroll
+            for (int kd = 0; kd < KD; ++kd) {
+                s[rb] = mm::mma(bw_arow<D>(qt_, row, 4 * kd + gq), kop[kd], s[rb]);
+                dp[rb] = mm::mma(bw_arow<D>(dt_, row, 4 * kd + gq), vop[kd], dp[rb]);
+            }
+        }
+        float p[16], ds[16];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const int r0 = 32 * (rb >> 1) + 8 * gq + 4 * (rb & 1);   // tile rows r0 .. r0 + 3
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_l[buf][r0]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dl[buf][r0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = i0 + r0 + e;
+                const bool vis = j < g.skv && j >= fa_row_lo(g, i) && j <= fa_row_hi(g, i);
+                const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - l4[e])
+                                     : 0.f;
+                p[4 * rb + e] = pv;
+                ds[4 * rb + e] = pv * (dp[rb][e] - d4[e]);
+            }
+        }
+        u32x4 pop[2], dsop[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const float* pl = p + 8 * kk;
+            const float* dl = ds + 8 * kk;
+            pop[kk] = u32x4{io::pack(pl[0], pl[1]), io::pack(pl[2], pl[3]), io::pack(pl[4], pl[5]), io::pack(pl[6], pl[7])};
+            dsop[kk] = u32x4{io::pack(dl[0], dl[1]), io::pack(dl[2], dl[3]), io::pack(dl[4], dl[5]), io::pack(dl[6], dl[7])};
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                dv[db] = mm::mma(pop[kk], bw_bcol<D>(dt_, kk, db, gq, n), dv[db]);
+                dk[db] = mm::mma(dsop[kk], bw_bcol<D>(qt_, kk, db, gq, n), dk[db]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        if (tid < BW_T) {
+            lds_l[buf ^ 1][tid] = l2n;
+            lds_dl[buf ^ 1][tid] = dln;
+        }
+        __syncthreads();
+    }
+#undef BW_LOAD_Q
+    // Keys 16 wave + 4 gq + e, columns 16 db + n.
+    uint16_t* dkp = static_cast<uint16_t*>(a.dk) + ko;
+    uint16_t* dvp = static_cast<uint16_t*>(a.dv) + ko;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int key = j0 + 16 * wave + 4 * gq + e;
+        if (key < g.skv) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dkp[int64_t(key) * kv_rs + 16 * db + n] = uint16_t(io::pack(dk[db][e] * a.scale, 0.f) & 0xffffu);
+                dvp[int64_t(key) * kv_rs + 16 * db + n] = uint16_t(io::pack(dv[db][e], 0.f) & 0xffffu);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Host side.
+// ------------------------------------------------------------------------------------------
+
+struct bw_plan {
+    fa_plan p;
+    bool mfma = false;
+    int32_t n_qt = 0, n_kt = 0;
+    size_t ws_delta_offset = 0, ws_bytes = 0;
+    int64_t lse_elems = 0;
+};
+
+fa_status make_bw_plan(const fa_call& c, bool sizes_only, bw_plan* out) {
+    bw_plan bp;
+    const fa_status st = sizes_only ? fa_make_plan_sizes(c, &bp.p) : fa_make_plan(c, false, &bp.p);
+    if (st != FA_OK) return st;
+    const fa_dims& d = *c.dims;
+    const fa_plan& p = bp.p;
+    int64_t max_sq = 0, max_skv = 0;
+    if (c.layout == FA_LAYOUT_TND) {
+        int64_t pq = 0, pk = 0;
+        for (int64_t b = 0; b < d.B; ++b) {
+            max_sq = std::max(max_sq, c.actual_seq_qlen[b] - pq);
+            max_skv = std::max(max_skv, c.actual_seq_kvlen[b] - pk);
+            pq = c.actual_seq_qlen[b];
+            pk = c.actual_seq_kvlen[b];
+        }
+        bp.lse_elems = d.N * d.T_q;
+    } else {
+        max_sq = d.Sq;
+        max_skv = d.Skv;
+        bp.lse_elems = d.B * d.N * d.Sq;
+    }
+    bp.n_qt = int32_t((max_sq + BW_T - 1) / BW_T);
+    bp.n_kt = int32_t((max_skv + BW_T - 1) / BW_T);
+    bp.mfma = (d.dtype == FA_DTYPE_F16 || d.dtype == FA_DTYPE_BF16) && (d.D == 64 || d.D == 128) &&
+              c.sparse_mode != 1 && d.N * d.D * 2 * 256 < (int64_t(1) << 31);
+    size_t off = 0;
+    if (p.table) off = (size_t(d.B) * sizeof(fa_geom) + 255) & ~size_t(255);
+    bp.ws_delta_offset = off;
+    off += size_t(bp.lse_elems) * sizeof(float);
+    bp.ws_bytes = (p.rows_total == 0 && p.kv_total == 0) ? 0 : ((off + 255) & ~size_t(255));
+    *out = std::move(bp);
+    return FA_OK;
+}
+
+template <typename T, int DMAX, bool DENSE, int AL>
+void launch_generic(const fa_bwd_args& a, int64_t pairs, hipStream_t s) {
+    const int nq = (a.n_qt * BW_T + GB_ROWS - 1) / GB_ROWS, nk = (a.n_kt * BW_T + GB_ROWS - 1) / GB_ROWS;
+    if (nk > 0) {
+        fa_bwd_dkdv_generic<T, DMAX, DENSE, AL, 0><<<dim3(unsigned(pairs * nk)), dim3(GB_ROWS), 0, s>>>(a);
+        fa_bwd_dkdv_generic<T, DMAX, DENSE, AL, 1><<<dim3(unsigned(pairs * nk)), dim3(GB_ROWS), 0, s>>>(a);
+    }
+    if (nq > 0) fa_bwd_dq_generic<T, DMAX, DENSE, AL><<<dim3(unsigned(pairs * nq)), dim3(GB_ROWS), 0, s>>>(a);
+}
+
+template <typename T, int DMAX>
+void launch_generic_d(const fa_bwd_args& a, int al, bool dense, int64_t pairs, hipStream_t s) {
+    switch (al * 2 + (dense ? 1 : 0)) {
+        case 0: launch_generic<T, DMAX, false, 0>(a, pairs, s); break;
+        case 1: launch_generic<T, DMAX, true, 0>(a, pairs, s); break;
+        case 2: launch_generic<T, DMAX, false, 1>(a, pairs, s); break;
+        case 3: launch_generic<T, DMAX, true, 1>(a, pairs, s); break;
+        case 4: launch_generic<T, DMAX, false, 2>(a, pairs, s); break;
+        default: launch_generic<T, DMAX, true, 2>(a, pairs, s); break;
+    }
+}
+
+template <typename T>
+void launch_generic_t(const fa_bwd_args& a, int al, bool dense, int64_t pairs, hipStream_t s) {
+    if (a.D <= 32) launch_generic_d<T, 32>(a, al, dense, pairs, s);
+    else if (a.D <= 64) launch_generic_d<T, 64>(a, al, dense, pairs, s);
+    else launch_generic_d<T, 128>(a, al, dense, pairs, s);
+}
+
+template <int D, bool BF, int AL>
+void launch_mfma(const fa_bwd_args& a, int64_t pairs, hipStream_t s) {
+    if (a.n_kt > 0) fa_bwd_dkdv_mfma<D, BF, AL><<<dim3(unsigned(pairs * a.n_kt)), dim3(BW_THREADS), 0, s>>>(a);
+    if (a.n_qt > 0) fa_bwd_dq_mfma<D, BF, AL><<<dim3(unsigned(pairs * a.n_qt)), dim3(BW_THREADS), 0, s>>>(a);
+}
+
+template <int D, bool BF>
+void launch_mfma_al(const fa_bwd_args& a, int al, int64_t pairs, hipStream_t s) {
+    switch (al) {
+        case 0: launch_mfma<D, BF, 0>(a, pairs, s); break;
+        case 1: launch_mfma<D, BF, 1>(a, pairs, s); break;
+        default: launch_mfma<D, BF, 2>(a, pairs, s); break;
+    }
+}
+
+fa_call bw_call(const fa_dims* dims, int32_t layout, int32_t sparse_mode, int64_t pre, int64_t next,
+                const int64_t* qlen, const int64_t* kvlen, const int64_t* prefix, bool alibi, int32_t alibi_mode,
+                bool mask, const int64_t* mask_bcast, float scale) {
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = sparse_mode;
+    c.pre_tokens = pre;
+    c.next_tokens = next;
+    c.actual_seq_qlen = qlen;
+    c.actual_seq_kvlen = kvlen;
+    c.prefix = prefix;
+    c.has_alibi = alibi;
+    c.alibi_mode = alibi_mode;
+    c.has_mask = mask;
+    c.mask_bcast = mask_bcast;
+    c.scale = scale;
+    return c;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_bwd_workspace_size(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                                           const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                                           size_t* bytes) {
+    if (!dims || !bytes) return FA_ERR_NULLPTR;
+    const fa_call c = bw_call(dims, layout, sparse_mode, 0, 0, actual_seq_qlen, actual_seq_kvlen, nullptr, false,
+                              FA_ALIBI_RIGHT, false, nullptr, 1.f);
+    bw_plan bp;
+    const fa_status st = make_bw_plan(c, true, &bp);
+    if (st != FA_OK) return st;
+    *bytes = bp.ws_bytes;
+    return FA_OK;
+}
+
+extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* softmax_lse,
+                            const void* dout, void* dq, void* dk, void* dv, const fa_dims* dims, int32_t layout,
+                            int32_t sparse_mode, int64_t pre_tokens, int64_t next_tokens,
+                            const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen, const int64_t* prefix,
+                            const float* alibi_slopes, int32_t alibi_mode, const uint8_t* atten_mask,
+                            const int64_t* mask_bcast, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    const fa_call c = bw_call(dims, layout, sparse_mode, pre_tokens, next_tokens, actual_seq_qlen, actual_seq_kvlen,
+                              prefix, alibi_slopes != nullptr, alibi_mode, atten_mask != nullptr, mask_bcast, scale);
+    bw_plan bp;
+    fa_status st = make_bw_plan(c, false, &bp);
+    if (st != FA_OK) return st;
+    const fa_plan& p = bp.p;
+    if (p.rows_total > 0 && (!q || !out || !softmax_lse || !dout || !dq)) return FA_ERR_NULLPTR;
+    if (p.kv_total > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULLPTR;
+    if (bp.ws_bytes > 0) {
+        if (!workspace) return FA_ERR_NULLPTR;
+        if (workspace_bytes < bp.ws_bytes) return FA_ERR_WORKSPACE;
+    }
+    const int64_t pairs = int64_t(p.B) * p.N;
+    if (pairs * std::max<int64_t>(int64_t(std::max(bp.n_qt, bp.n_kt)) * (BW_T / DL_ROWS), 1) >= (int64_t(1) << 31))
+        return FA_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    // Every dK / dV row of a sequence with keys is written (zeros where no query sees the key),
+    // also when there are no query rows at all.
+    if (p.kv_total == 0 && p.rows_total == 0) return FA_OK;
+    if (p.table) {
+        if (hipMemcpyAsync(workspace, p.geoms.data(), p.geoms.size() * sizeof(fa_geom), hipMemcpyHostToDevice, s) !=
+            hipSuccess)
+            return FA_ERR_HIP;
+    }
+    fa_bwd_args a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = out;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.lse = softmax_lse;
+    a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + bp.ws_delta_offset);
+    a.slopes = alibi_slopes;
+    a.mask = atten_mask;
+    a.geoms = p.table ? static_cast<const fa_geom*>(workspace) : nullptr;
+    a.geom0 = p.geom0;
+    a.q_bs = p.q_bs; a.q_hs = p.q_hs; a.q_rs = p.q_rs;
+    a.kv_bs = p.kv_bs; a.kv_hs = p.kv_hs; a.kv_rs = p.kv_rs;
+    a.lse_bs = p.lse_bs; a.lse_hs = p.lse_hs;
+    a.m_bs = p.m_bs; a.m_hs = p.m_hs; a.m_rs = p.m_rs;
+    a.B = p.B;
+    a.N = p.N;
+    a.D = p.D;
+    a.n_qt = bp.n_qt;
+    a.n_kt = bp.n_kt;
+    a.alibi_left = alibi_mode == FA_ALIBI_LEFT ? 1 : 0;
+    a.scale_log2 = scale * kLog2e;
+    a.scale = scale;
+    const int al = alibi_slopes == nullptr ? 0 : (alibi_mode == FA_ALIBI_SQRT ? 2 : 1);
+    const bool dense = sparse_mode == 1;
+    const int32_t dtype = dims->dtype;
+    if (bp.n_qt > 0) {
+        const dim3 grid(unsigned(pairs * ((bp.n_qt * BW_T + DL_ROWS - 1) / DL_ROWS)));
+        switch (dtype) {
+            case FA_DTYPE_F32: fa_bwd_delta<float><<<grid, dim3(BW_THREADS), 0, s>>>(a); break;
+            case FA_DTYPE_F16: fa_bwd_delta<_Float16><<<grid, dim3(BW_THREADS), 0, s>>>(a); break;
+            default: fa_bwd_delta<__bf16><<<grid, dim3(BW_THREADS), 0, s>>>(a); break;
+        }
+    }
+    if (bp.mfma) {
+        const bool bf = dtype == FA_DTYPE_BF16;
+        if (p.D == 128) {
+            if (bf) launch_mfma_al<128, true>(a, al, pairs, s);
+            else launch_mfma_al<128, false>(a, al, pairs, s);
+        } else {
+            if (bf) launch_mfma_al<64, true>(a, al, pairs, s);
+            else launch_mfma_al<64, false>(a, al, pairs, s);
+        }
+    } else {
+        switch (dtype) {
+            case FA_DTYPE_F32: launch_generic_t<float>(a, al, dense, pairs, s); break;
+            case FA_DTYPE_F16: launch_generic_t<_Float16>(a, al, dense, pairs, s); break;
+            default: launch_generic_t<__bf16>(a, al, dense, pairs, s); break;
+        }
+    }
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    return FA_OK;
+}

@@ -39,13 +39,11 @@
 #include <cstdlib>
 #include <vector>
 
+#include "fa_device.h"
 #include "fa_mask.h"
 #include "fa_plan.h"
 
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 struct fa_kargs {
     const void* q;
@@ -77,24 +75,12 @@ struct fa_kargs {
     int32_t num_pages;            // valid page ids are [0, num_pages)
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
 // Work item of this workgroup. Workgroups are dispatched round-robin over the 8 XCDs, each
 // with its own L2. Table mode (varlen / prefix): heads are the fastest index, so the blocks
 // of one (batch, head) share an XCD when N is a multiple of 8, and items run heaviest first
 // (the planner sorted the table). Fixed-length mode with xcd_major: XCD x = blockIdx % 8
 // works through the (batch, head) pairs congruent to x one pair at a time, heaviest q tile
 // first, so each XCD streams the K/V of about one pair through its L2 at a time.
-// Values read from the workspace tables are the same for every lane; readfirstlane keeps them
-// in scalar registers (buffer descriptors built from them must be wave-uniform).
-__device__ __forceinline__ int fa_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ fa_geom fa_geom_of(const fa_kargs& a, int b) {
     if (!a.geoms) return a.geom0;
@@ -138,51 +124,12 @@ __device__ __forceinline__ void fa_decode_item(const fa_kargs& a, int& b, int& h
 // MFMA kernel
 // ------------------------------------------------------------------------------------------
 
-template <bool IS_BF16>
-struct mfma_io;
-
-template <>
-struct mfma_io<true> {
-    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ uint32_t pack(float x, float y) {
-        bf16x2 r;
-        r.x = (__bf16)x;
-        r.y = (__bf16)y;
-        return __builtin_bit_cast(uint32_t, r);
-    }
-};
-
-template <>
-struct mfma_io<false> {
-    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ uint32_t pack(float x, float y) {
-        f16x2 r;
-        r.x = (_Float16)x;
-        r.y = (_Float16)y;
-        return __builtin_bit_cast(uint32_t, r);
-    }
-};
-
 // LDS index (in 16-byte chunks) of chunk c of row r, for rows of 16 chunks (256 bytes).
 __device__ __forceinline__ int lds_idx16(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 // Same for rows of 8 chunks (128 bytes): two rows share a 256-byte line.
 __device__ __forceinline__ int lds_idx8(int r, int c) {
     const int line = r >> 1;
     return line * 16 + ((8 * (r & 1) + c) ^ (line & 7));
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t fa_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 fa_bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
 // max / sum of x over the lane pair (l, l ^ 32); both lanes get the same bits.
@@ -195,8 +142,6 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // K and V tiles live in LDS row-major (a row is D/8 chunks of 16 bytes); chunk c of row j
 // sits at c ^ swz(j). D = 128 (256-byte rows): swz swaps the two 2-bit fields of j & 15, a
@@ -1026,29 +971,6 @@ fa_fwd_pp(const fa_kargs a) {
 constexpr int DC_THREADS = 256;
 constexpr int DC_BN = FA_DEC_BN;     // keys per tile
 constexpr int DC_ROWS = FA_DEC_ROWS; // query rows (the MFMA's 16 columns)
-
-// s_waitcnt immediate for vmcnt(n), n < 64 (vmcnt bits 3:0 and 15:14; the other counters
-// left at their maxima).
-constexpr int fa_vmcnt64(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-template <bool IS_BF16>
-struct mfma16_io;
-
-template <>
-struct mfma16_io<true> {
-    static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-};
-
-template <>
-struct mfma16_io<false> {
-    static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-};
 
 struct fa_decode_args {
     float* o_part;     // [B N n_split, 16, D]: each split's O / l (n_split > 1)

@@ -433,3 +433,41 @@ def test_decode_plan_split_counts(lib):
     ws = fb.fa_fwd_workspace_size(d, "TND", 3, [1, 1, 17], [9000, 9005, 9005])
     n_split = max(1, min(-(-1024 // (3 * 2)), -(-9000 // 64) // 8))
     assert ws == _align256(3 * 32) + _align256(3 * 2 * n_split * 16 * 128 * 4) + _align256(3 * 2 * n_split * 16 * 4)
+
+
+# ---------------------------------------------------------------------------------------
+# Backward: host validation (no device work)
+# ---------------------------------------------------------------------------------------
+
+def test_bwd_validation_and_workspace(lib):
+    """fa_bwd applies fa_fwd's argument rules before any launch and needs its own pointers;
+    its workspace holds Delta (fp32, laid out like softmax_lse) after the per-batch geometry
+    (TND / prefix modes)."""
+    buf = (ctypes.c_char * 4096)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    d = bnsd(B=2, N=4, Sq=64, Skv=80, D=128)
+
+    def call(dims=d, mode=3, pre=0, nxt=0, q=p, dq=p, dk=p, lse=p, scale=0.125, ws=p, wsb=4096, alibi_mode=0):
+        return lib.fa_bwd(q, p, p, p, lse, p, dq, dk, p, ctypes.byref(dims), 0, mode, pre, nxt, None, None, None,
+                          None, alibi_mode, None, None, scale, ws, wsb, None)
+
+    assert call(q=None) == NULLPTR
+    assert call(dq=None) == NULLPTR
+    assert call(dk=None) == NULLPTR
+    assert call(lse=None) == NULLPTR
+    assert call(mode=9) == INVALID
+    assert call(mode=4, pre=3, nxt=-9) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(alibi_mode=5) == INVALID
+    assert call(dims=bnsd(D=129)) == UNSUPPORTED
+    need = fb.fa_bwd_workspace_size(d, "BNSD", 3)
+    assert need == _align256(2 * 4 * 64 * 4)
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=None, wsb=0) == NULLPTR
+    dt = tnd([3, 0, 9], [5, 7, 0])
+    need_t = fb.fa_bwd_workspace_size(dt, "TND", 3, [3, 3, 12], [5, 12, 12])
+    assert need_t == _align256(3 * 32) + _align256(2 * 12 * 4)
+    # nothing at all to do: OK without pointers
+    d0 = bnsd(B=0)
+    assert lib.fa_bwd(None, None, None, None, None, None, None, None, None, ctypes.byref(d0), 0, 3, 0, 0, None, None,
+                      None, None, 0, None, None, 0.125, None, 0, None) == OK
