@@ -177,6 +177,55 @@ def paged_caches(w, k, v, bs, cache_layout, dev):
     return caches[0], caches[1], torch.from_numpy(bt).to(dev)
 
 
+def bench_bwd(args, dev):
+    """Backward pass of the workload: fa_fwd once for out and softmax_lse, then fa_bwd timed
+    alone with a seeded dO. Effective TFLOP/s count 10 D flops per visible pair, the five
+    products of the backward (S recomputed, dP, dV, dK, dQ)."""
+    import torch
+    from masked_attention_forward_amd import binding as fb
+    from masked_attention_forward_amd import synth
+
+    w = synth.workloads()[args.workload]
+    q, k, v = (x.to(dev) for x in w.tensors())
+    do = synth.randn(tuple(q.shape), q.dtype, w.seed * 3 + 7).to(dev)
+    slopes = torch.tensor(w.slopes(), dtype=torch.float32, device=dev) if w.alibi else None
+    kw = dict(layout=w.layout, sparse_mode=w.sparse_mode, pre_tokens=w.pre_tokens, next_tokens=w.next_tokens,
+              actual_seq_qlen=w.actual_seq_qlen, actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix,
+              alibi_slopes=slopes, alibi_mode=args.alibi_mode, scale=w.softmax_scale)
+    out, lse = fb.flash_attention(q, k, v, **kw)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dims = fb.dims_of(q, k, w.layout, w.actual_seq_qlen)
+    ws_bytes = fb.fa_bwd_workspace_size(dims, w.layout, w.sparse_mode, w.actual_seq_qlen, w.actual_seq_kvlen)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        fb.fa_bwd(q, k, v, out, lse, do, dq, dk, dv, workspace=ws if ws_bytes else None, **kw)
+
+    pairs = visible_pairs(w, dev)
+    flops = 10 * w.D * pairs
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "effective TFLOP/s attn bwd (10 D flops per visible pair)", "value": round(tflops, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f16": "f16", "f32": "f32"}[w.dtype], "data": "synthetic (seeded N(0,1) q/k/v/dO)",
+        "config": {"workload": args.workload, "layout": w.layout, "sparse_mode": w.sparse_mode, "B": w.B, "N": w.N,
+                   "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "visible_pairs": pairs, "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}}), flush=True)
+
+
 def bench_scatter(args, dev):
     """Paged KV cache scatter ("aclnnScatterPaKvCache", Norm cache): a prefill chunk of
     32768 tokens x 32 heads x D 128 bf16 keys and values written to random distinct slots of a
@@ -231,8 +280,8 @@ def main():
                     help="alibi variant for workloads with alibi")
     ap.add_argument("--cpu-heads", type=int, default=48,
                     help="(batch, head) slices of the workload the CPU oracle is timed on")
-    ap.add_argument("--op", default="attention", choices=["attention", "scatter_kv"],
-                    help="attention (the default metric) or the paged KV cache scatter")
+    ap.add_argument("--op", default="attention", choices=["attention", "scatter_kv", "bwd"],
+                    help="attention (the default metric), the paged KV cache scatter, or the backward pass")
     ap.add_argument("--block-size", type=int, default=0,
                     help="> 0: read K / V through fa_fwd_paged from caches of pages of this many keys")
     ap.add_argument("--cache-layout", default="Norm", choices=["Norm", "NHSD"],
@@ -262,6 +311,9 @@ def main():
         return
     if args.op == "scatter_kv":
         bench_scatter(args, dev)
+        return
+    if args.op == "bwd":
+        bench_bwd(args, dev)
         return
     w = synth.workloads()[args.workload]
     q, k, v = (x.to(dev) for x in w.tensors())

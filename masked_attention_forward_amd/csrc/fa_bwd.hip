@@ -417,13 +417,16 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args a
             }
         }
         const int j0 = kt * BW_T;
+        // Every (row, key) of this wave's 16 rows x 64 keys visible: no per-element test.
+        const bool full = fa_tile_full(g, i0 + 16 * wave, min(i0 + 16 * wave + 15, g.sq - 1), j0, BW_T) &&
+                          i0 + 16 * wave + 15 < g.sq;
         float ds[16];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = j0 + 32 * (bb >> 1) + 8 * gq + 4 * (bb & 1) + e;
-                const bool vis = row_ok && j >= row_lo && j <= row_hi;
+                const bool vis = full || (row_ok && j >= row_lo && j <= row_hi);
                 const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[bb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - lse2)
                                     : 0.f;
                 ds[4 * bb + e] = p * (dp[bb][e] - dlt);
@@ -549,6 +552,8 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args
                 dp[rb] = mm::mma(bw_arow<D>(dt_, row, 4 * kd + gq), vop[kd], dp[rb]);
             }
         }
+        // Every (row, key) of the 64 rows x this wave's 16 keys visible: no per-element test.
+        const bool full = i0 + BW_T <= g.sq && fa_tile_full(g, i0, i0 + BW_T - 1, j0 + 16 * wave, 16);
         float p[16], ds[16];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
@@ -558,7 +563,7 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = i0 + r0 + e;
-                const bool vis = j < g.skv && j >= fa_row_lo(g, i) && j <= fa_row_hi(g, i);
+                const bool vis = full || (j < g.skv && j >= fa_row_lo(g, i) && j <= fa_row_hi(g, i));
                 const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - l4[e])
                                      : 0.f;
                 p[4 * rb + e] = pv;
