@@ -106,9 +106,12 @@ __device__ __forceinline__ void fa_decode_item(const fa_kargs& a, int& b, int& h
         b = fa_uniform(a.items[2 * item]);
         qt = fa_uniform(a.items[2 * item + 1]);
     } else if (a.xcd_major) {
+        // Pair-major (1): the pairs of XCD x one after another, each heaviest q tile first.
+        // Rank-major (2): the heaviest q tile of every pair of XCD x, then the next rank.
         const int x = w & 7, slot = w >> 3;
-        const int pair = (slot / a.n_qtiles_fixed) * 8 + x;
-        const int r = slot % a.n_qtiles_fixed;
+        const int ppx = a.B * a.N / 8;
+        const int pair = (a.xcd_major == 2 ? slot % ppx : slot / a.n_qtiles_fixed) * 8 + x;
+        const int r = a.xcd_major == 2 ? slot / ppx : slot % a.n_qtiles_fixed;
         b = pair / a.N;
         h = pair % a.N;
         qt = a.reverse_qt ? a.n_qtiles_fixed - 1 - r : r;

@@ -17,6 +17,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
+#include <queue>
 
 namespace {
 
@@ -374,6 +376,38 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
             p.reverse_qt = item_cost(0, p.n_qtiles_fixed - 1, nullptr) > item_cost(0, 0, nullptr);
         const char* xm = std::getenv("FA_XCD_MAJOR");
         p.xcd_major = ((B * d.N) % 8 == 0 && !(xm && xm[0] == '0')) ? 1 : 0;
+        if (p.xcd_major && !sizes_only && p.kernel != FA_KERNEL_DECODE) {
+            // Model one XCD's dispatch (every XCD sees the same pattern): its 32 CUs take the
+            // next workgroup in launch order when free; an item costs its kv tiles plus a fixed
+            // two. Pair-major order (one (batch, head) after another, heaviest q tile first) keeps
+            // one pair's K/V in the XCD's L2; rank-major (the heaviest q tile of every pair, then
+            // the next) balances better when a pair has few, very unequal q tiles. Take rank-major
+            // when the model says it finishes more than 5% sooner (FA_XCD_ORDER=pair|rank forces).
+            const int64_t ppx = B * d.N / 8;
+            const int32_t nq = p.n_qtiles_fixed;
+            const int slots = 32 * ((p.kernel == FA_KERNEL_PP && d.D == 128) ? 1 : 2);
+            std::vector<int64_t> cost(nq);
+            for (int32_t r = 0; r < nq; ++r)
+                cost[r] = item_cost(0, p.reverse_qt ? nq - 1 - r : r, nullptr) + 2;
+            auto makespan = [&](bool rank_major) {
+                std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+                for (int i = 0; i < slots; ++i) free_at.push(0);
+                int64_t end = 0;
+                for (int64_t sl = 0; sl < ppx * nq; ++sl) {
+                    const int32_t r = rank_major ? int32_t(sl / ppx) : int32_t(sl % nq);
+                    const int64_t t = free_at.top() + cost[r];
+                    free_at.pop();
+                    free_at.push(t);
+                    end = std::max(end, t);
+                }
+                return end;
+            };
+            bool rank = ppx > 1 && nq > 1 && makespan(true) * 20 < makespan(false) * 19;
+            const char* xo = std::getenv("FA_XCD_ORDER");
+            if (xo && std::strcmp(xo, "rank") == 0) rank = true;
+            if (xo && std::strcmp(xo, "pair") == 0) rank = false;
+            if (rank) p.xcd_major = 2;
+        }
     }
 
     if (with_tables && !sizes_only) {

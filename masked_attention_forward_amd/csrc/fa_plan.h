@@ -64,7 +64,8 @@ struct fa_plan {
     int64_t n_items = 0;        // work items per head
     int32_t n_qtiles_fixed = 0; // q tiles per batch (fixed-length mode)
     int32_t reverse_qt = 0;     // fixed-length mode: launch the last q tiles first
-    int32_t xcd_major = 0;      // fixed-length mode: XCD-major launch order (B * N % 8 == 0)
+    int32_t xcd_major = 0;      // fixed-length mode, B * N % 8 == 0: XCD-major launch order,
+                                // 1 = pair-major, 2 = rank-major (see fa_decode_item)
     int64_t n_qtiles_total = 0; // batch-major q tiles over all batches
     int64_t n_kvtiles_max = 0;
     size_t ws_bytes = 0;
