@@ -376,7 +376,7 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
             p.reverse_qt = item_cost(0, p.n_qtiles_fixed - 1, nullptr) > item_cost(0, 0, nullptr);
         const char* xm = std::getenv("FA_XCD_MAJOR");
         p.xcd_major = ((B * d.N) % 8 == 0 && !(xm && xm[0] == '0')) ? 1 : 0;
-        if (p.xcd_major && !sizes_only && p.kernel != FA_KERNEL_DECODE) {
+        if (p.xcd_major && B > 0 && !sizes_only && p.kernel != FA_KERNEL_DECODE) {
             // Model one XCD's dispatch (every XCD sees the same pattern): its 32 CUs take the
             // next workgroup in launch order when free; an item costs its kv tiles plus a fixed
             // two. Pair-major order (one (batch, head) after another, heaviest q tile first) keeps
