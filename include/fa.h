@@ -183,11 +183,12 @@ fa_status fa_tile_shape(const fa_dims* dims, int32_t layout, const int64_t* actu
                         int64_t* n_qtiles_total, int64_t* n_kvtiles_max);
 
 /* Host-side plan summary of one fa_fwd call (same validation as fa_fwd, no device work).
- * kernel: 0 = generic, 1 = MFMA. Tile counts are per head. */
+ * kernel: 0 = generic, 1 = ping-pong MFMA, 2 = four-wave MFMA, 3 = split-KV decode. Tile
+ * counts are per head. */
 typedef struct fa_plan_stats {
     int32_t kernel;
     int32_t block_m, block_n;
-    int64_t work_items;        /* (batch, q tile) pairs, per head                       */
+    int64_t work_items;        /* (batch, q tile) pairs per head; (batch, kv split) for 3 */
     int64_t kv_tiles_visited;  /* kv tiles loaded, summed over work items, per head     */
     int64_t kv_tiles_full;     /* of which need no per-element masking                  */
     int64_t kv_tiles_total;    /* kv tiles a dense pass would load, per head            */

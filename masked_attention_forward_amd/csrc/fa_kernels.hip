@@ -976,10 +976,37 @@ constexpr int DC_BN = FA_DEC_BN;     // keys per tile
 constexpr int DC_ROWS = FA_DEC_ROWS; // query rows (the MFMA's 16 columns)
 
 struct fa_decode_args {
-    float* o_part;     // [B N n_split, 16, D]: each split's O / l (n_split > 1)
-    float* lse_part;   // [B N n_split, 16]: each split's log2(sum) + max, log2 domain
-    int32_t n_split;
+    float* o_part;          // [split slots, N, 16, D]: each split's O / l (batches with splits)
+    float* lse_part;        // [split slots, N, 16]: each split's log2(sum) + max, log2 domain
+    const int32_t* batch;   // table mode: per batch (first slot, splits); else nullptr
+    int32_t n_split;        // fixed-length mode: splits of every batch
 };
+
+// Work of decode workgroup w: entry e = w / N (a (batch, split) pair), head w % N; the
+// batch's split count and its first partial-result slot. Slot (base + split) * N + h holds
+// this workgroup's partial result when ns > 1.
+struct fa_dec_work {
+    int b, h, split, ns, base;
+};
+
+__device__ __forceinline__ fa_dec_work fa_decode_work(const fa_kargs& a, const fa_decode_args& dc, int w) {
+    fa_dec_work r;
+    r.h = w % a.N;
+    const int e = w / a.N;
+    if (a.items) {
+        typedef const __attribute__((address_space(4))) int32_t* cptr;
+        r.b = fa_uniform(((cptr)a.items)[2 * e]);
+        r.split = fa_uniform(((cptr)a.items)[2 * e + 1]);
+        r.base = fa_uniform(((cptr)dc.batch)[2 * r.b]);
+        r.ns = fa_uniform(((cptr)dc.batch)[2 * r.b + 1]);
+    } else {
+        r.b = e / dc.n_split;
+        r.split = e % dc.n_split;
+        r.ns = dc.n_split;
+        r.base = r.b * dc.n_split;
+    }
+    return r;
+}
 
 template <int D, bool IS_BF16, int AL, bool PAGED>
 __global__ __launch_bounds__(DC_THREADS) void fa_decode_split(const fa_kargs a, const fa_decode_args dc) {
@@ -1000,16 +1027,14 @@ __global__ __launch_bounds__(DC_THREADS) void fa_decode_split(const fa_kargs a, 
     const int n = lane & 15;    // query row (S^T column / P and O row block index)
     const int gq = lane >> 4;   // 16-lane group
 
-    const int w = blockIdx.x;
-    const int split = w % dc.n_split;
-    const int bh = w / dc.n_split;
-    const int h = bh % a.N, b = bh / a.N;
+    const fa_dec_work wk = fa_decode_work(a, dc, blockIdx.x);
+    const int b = wk.b, h = wk.h, split = wk.split;
     const fa_geom g = fa_geom_of(a, b);
     if (g.sq <= 0) return;
     const int rows = min(g.sq, DC_ROWS);
     const fa_kv_range kr = fa_tile_kv_range(g, 0, rows - 1, DC_BN);
     const int n_tiles = kr.end - kr.begin;
-    const int tps = (n_tiles + dc.n_split - 1) / dc.n_split;
+    const int tps = (n_tiles + wk.ns - 1) / wk.ns;
     const int t0 = min(kr.begin + split * tps, kr.end);
     const int t1 = min(t0 + tps, kr.end);
     const int kv_lim = min(kr.end * DC_BN, g.skv);
@@ -1232,47 +1257,71 @@ __global__ __launch_bounds__(DC_THREADS) void fa_decode_split(const fa_kargs a, 
         }
         const float o = L > 0.f ? O / L : 0.f;
         const float lse2 = L > 0.f ? M + log2f(L) : -INFINITY;
-        if (dc.n_split == 1) {
+        if (wk.ns == 1) {
             uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.q_bs + h * a.q_hs + (int64_t(g.q_start) + r) * a.q_rs;
             const uint32_t pk = io::pack(o, 0.f);
             op[d] = uint16_t(pk & 0xffffu);
             if (d == 0) a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + r] = lse2 * kLn2;
         } else {
-            const int64_t slot = int64_t(bh) * dc.n_split + split;
+            const int64_t slot = int64_t(wk.base + split) * a.N + h;
             dc.o_part[(slot * DC_ROWS + r) * D + d] = o;
             if (d == 0) dc.lse_part[slot * DC_ROWS + r] = lse2;
         }
     }
 }
 
-// Combines the splits of fa_decode_split: one workgroup per (batch, head), one thread per
-// column.
-template <typename T>
-__global__ __launch_bounds__(128) void fa_decode_merge(const fa_kargs a, const fa_decode_args dc) {
+// Combines the splits of fa_decode_split: one workgroup per (batch, head), which returns at
+// once when the batch has one split (fa_decode_split wrote its output); thread t takes row
+// t / 16 and D / 16 consecutive columns, so every row and column is merged at once and each
+// thread's loads over the splits are independent of one another.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fa_decode_merge(const fa_kargs a, const fa_decode_args dc) {
+    constexpr int CPT = D / 16;   // columns per thread
     const int bh = blockIdx.x;
     const int h = bh % a.N, b = bh / a.N;
+    int ns = dc.n_split, base = b * dc.n_split;
+    if (dc.batch) {
+        base = dc.batch[2 * b];
+        ns = dc.batch[2 * b + 1];
+    }
+    if (ns <= 1) return;
     const fa_geom g = fa_geom_of(a, b);
     const int rows = min(g.sq, DC_ROWS);
-    const int d = threadIdx.x;
-    for (int r = 0; r < rows; ++r) {
-        float M = -INFINITY;
-        for (int sp = 0; sp < dc.n_split; ++sp) M = fmaxf(M, dc.lse_part[(int64_t(bh) * dc.n_split + sp) * DC_ROWS + r]);
-        float L = 0.f, O = 0.f;
-        if (M != -INFINITY) {
-            for (int sp = 0; sp < dc.n_split; ++sp) {
-                const int64_t slot = int64_t(bh) * dc.n_split + sp;
-                const float f = exp2f(dc.lse_part[slot * DC_ROWS + r] - M);
-                L += f;
-                if (d < a.D) O = fmaf(dc.o_part[(slot * DC_ROWS + r) * a.D + d], f, O);
+    const int r = threadIdx.x >> 4, c0 = (threadIdx.x & 15) * CPT;
+    if (r >= rows) return;
+    // Split sp's partial result is slot (base + sp) * N + h: slots of one (batch, head) lie
+    // N * 16 rows apart.
+    const int64_t stride = int64_t(a.N) * DC_ROWS;
+    const float* lp = dc.lse_part + int64_t(base) * stride + int64_t(h) * DC_ROWS + r;
+    const float* opp = dc.o_part + (int64_t(base) * stride + int64_t(h) * DC_ROWS + r) * D + c0;
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, lp[sp * stride]);
+    float L = 0.f;
+    float O[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) O[j] = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 4
+        for (int sp = 0; sp < ns; ++sp) {
+            const float f = exp2f(lp[sp * stride] - M);
+            L += f;
+            const float4* src = reinterpret_cast<const float4*>(opp + sp * stride * D);
+#pragma unroll
+            for (int j = 0; j < CPT / 4; ++j) {
+                const float4 x = src[j];
+                O[4 * j + 0] = fmaf(x.x, f, O[4 * j + 0]);
+                O[4 * j + 1] = fmaf(x.y, f, O[4 * j + 1]);
+                O[4 * j + 2] = fmaf(x.z, f, O[4 * j + 2]);
+                O[4 * j + 3] = fmaf(x.w, f, O[4 * j + 3]);
             }
         }
-        const int64_t qrow = int64_t(g.q_start) + r;
-        if (d < a.D) {
-            T* op = static_cast<T*>(a.o) + b * a.q_bs + h * a.q_hs + qrow * a.q_rs;
-            op[d] = T(L > 0.f ? O / L : 0.f);
-        }
-        if (d == 0) a.lse[b * a.lse_bs + h * a.lse_hs + qrow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
     }
+    const int64_t qrow = int64_t(g.q_start) + r;
+    T* op = static_cast<T*>(a.o) + b * a.q_bs + h * a.q_hs + qrow * a.q_rs + c0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) op[j] = T(L > 0.f ? O[j] / L : 0.f);
+    if (c0 == 0) a.lse[b * a.lse_bs + h * a.lse_hs + qrow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1560,7 +1609,7 @@ fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v,
         if (workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
     }
     if (p.empty) return FA_OK;
-    const int64_t nblocks = p.n_items * p.N * p.n_split;
+    const int64_t nblocks = p.n_items * p.N;
     if (nblocks >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (log_enabled()) {
@@ -1588,7 +1637,9 @@ fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v,
     if (p.kernel == FA_KERNEL_DECODE) {
         fa_decode_args dc{};
         dc.n_split = p.n_split;
-        if (p.n_split > 1) {
+        if (p.table)
+            dc.batch = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + p.ws_dec_batch_offset);
+        if (p.dec_merge) {
             dc.o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_opart_offset);
             dc.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_lse_offset);
         }
@@ -1610,10 +1661,15 @@ fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v,
                 else launch_decode_d<64, false, false>(a, dc, alibi, grid, s);
             }
         }
-        if (p.n_split > 1) {
-            const dim3 mgrid(static_cast<unsigned>(p.n_items * p.N)), mblock(128);
-            if (bf) fa_decode_merge<__bf16><<<mgrid, mblock, 0, s>>>(a, dc);
-            else fa_decode_merge<_Float16><<<mgrid, mblock, 0, s>>>(a, dc);
+        if (p.dec_merge) {
+            const dim3 mgrid(static_cast<unsigned>(int64_t(p.B) * p.N)), mblock(256);
+            if (p.D == 128) {
+                if (bf) fa_decode_merge<__bf16, 128><<<mgrid, mblock, 0, s>>>(a, dc);
+                else fa_decode_merge<_Float16, 128><<<mgrid, mblock, 0, s>>>(a, dc);
+            } else {
+                if (bf) fa_decode_merge<__bf16, 64><<<mgrid, mblock, 0, s>>>(a, dc);
+                else fa_decode_merge<_Float16, 64><<<mgrid, mblock, 0, s>>>(a, dc);
+            }
         }
     } else if (p.kernel == FA_KERNEL_PP && p.paged) {
         const bool bf = dtype == FA_DTYPE_BF16;

@@ -320,26 +320,114 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         return r.end - r.begin;
     };
     if (p.kernel == FA_KERNEL_DECODE) {
-        // One work item per batch (all of its <= 16 rows); the kv range is split so that the
-        // launch has about FA_DEC_TARGET_WGS workgroups.
-        p.n_items = B;
-        const int64_t pairs = std::max<int64_t>(B * d.N, 1);
-        const int64_t max_tiles = ceil_div(max_skv, FA_DEC_BN);
-        const int64_t by_wgs = ceil_div(FA_DEC_TARGET_WGS, pairs);
-        const int64_t by_len = std::max<int64_t>(1, max_tiles / FA_DEC_MIN_TILES);
-        p.n_split = int32_t(std::max<int64_t>(1, std::min(by_wgs, by_len)));
+        // Split-KV decode: sequence b's kv tiles (by its length, not its visible range, so the
+        // workspace-size query plans the same) are cut into ns_b splits of at most C tiles, one
+        // workgroup per (split, head). C comes from a model of the launch: a workgroup costs
+        // its tiles plus FA_DEC_WG_COST, the chip holds FA_DEC_SLOTS of them at once (per CU,
+        // what the kernel's LDS allows), the makespan is the larger of the total cost over the
+        // slots and the longest workgroup (whole rounds when all are equal), and splitting adds
+        // the merge kernel's FA_DEC_MERGE_COST. Table mode (per-batch geometry) launches the
+        // (batch, split) entries longest first.
+        const int64_t slots = FA_DEC_SLOTS * (d.D == 64 ? 2 : 1);
+        std::vector<int64_t> tiles(B);
+        int64_t max_tiles = 0;
+        for (int64_t b = 0; b < B; ++b) {
+            tiles[b] = sq[b] > 0 ? ceil_div(skv[b], FA_DEC_BN) : 0;
+            max_tiles = std::max(max_tiles, tiles[b]);
+        }
+        auto splits_of = [](int64_t t, int64_t c) { return t <= c ? int64_t(1) : ceil_div(t, c); };
+        auto estimate = [&](int64_t c) {
+            double sum = 0.0, longest = 0.0, first = -1.0;
+            int64_t busy = 0;
+            bool split = false, equal = true;
+            for (int64_t b = 0; b < B; ++b) {
+                if (tiles[b] == 0) continue;
+                const int64_t ns = splits_of(tiles[b], c);
+                const double len = double(ceil_div(tiles[b], ns) + FA_DEC_WG_COST);
+                sum += double(d.N * ns) * len;
+                busy += d.N * ns;
+                longest = std::max(longest, len);
+                split = split || ns > 1;
+                if (first < 0.0) first = len;
+                equal = equal && len == first;
+            }
+            double t = std::max(sum / double(slots), longest);
+            if (equal && busy > 0) t = std::max(t, double(ceil_div(busy, slots)) * first);
+            return t + (split ? double(FA_DEC_MERGE_COST) : 0.0);
+        };
+        int64_t chunk = std::max<int64_t>(max_tiles, 1);
+        const char* ce = std::getenv("FA_DEC_CHUNK");   // tiles per split (comparisons)
+        if (ce) {
+            chunk = std::max<int64_t>(1, std::atoll(ce));
+        } else if (B * d.N < 8 * slots) {
+            // Fewer splits win ties: each candidate must beat the best so far by 1%.
+            double best = estimate(chunk);
+            for (int64_t k = 2; k <= FA_DEC_MAX_SPLITS; ++k) {
+                const int64_t c = ceil_div(max_tiles, k);
+                if (c < FA_DEC_MIN_TILES) break;
+                const double e = estimate(c);
+                if (e < 0.99 * best) {
+                    best = e;
+                    chunk = c;
+                }
+            }
+        }
+        // Entries, splits per batch and the partial-result slots of split batches.
+        std::vector<int32_t> ns_b(B);
+        int64_t entries = 0, split_slots = 0;
+        p.n_split = 1;
+        for (int64_t b = 0; b < B; ++b) {
+            ns_b[b] = int32_t(splits_of(tiles[b], chunk));
+            entries += ns_b[b];
+            if (ns_b[b] > 1) split_slots += ns_b[b];
+            p.n_split = std::max(p.n_split, ns_b[b]);
+        }
+        p.dec_merge = split_slots > 0;
+        p.n_items = entries;
         size_t off = 0;
-        if (p.table) off = align256(size_t(B) * sizeof(fa_geom));
-        p.ws_items_offset = off;
-        if (p.n_split > 1) {
-            const size_t slots = size_t(B) * size_t(d.N) * size_t(p.n_split) * FA_DEC_ROWS;
+        if (p.table) {
+            p.ws_items_offset = align256(size_t(B) * sizeof(fa_geom));
+            p.ws_dec_batch_offset = align256(p.ws_items_offset + size_t(entries) * 2 * sizeof(int32_t));
+            off = align256(p.ws_dec_batch_offset + size_t(B) * 2 * sizeof(int32_t));
+            p.ws_table_bytes = p.empty ? 0 : off;
+            if (with_tables && !sizes_only) {
+                std::vector<std::pair<int64_t, int64_t>> order;   // (tiles of the split, entry)
+                std::vector<int32_t> raw;
+                order.reserve(entries);
+                raw.reserve(2 * entries);
+                p.dec_batch.assign(2 * B, 0);
+                int32_t base = 0;
+                for (int64_t b = 0; b < B; ++b) {
+                    p.dec_batch[2 * b] = ns_b[b] > 1 ? base : 0;
+                    p.dec_batch[2 * b + 1] = ns_b[b];
+                    if (ns_b[b] > 1) base += ns_b[b];
+                    const int64_t len = ceil_div(tiles[b], ns_b[b]);
+                    for (int32_t sp = 0; sp < ns_b[b]; ++sp) {
+                        order.push_back({len, int64_t(raw.size() / 2)});
+                        raw.push_back(int32_t(b));
+                        raw.push_back(sp);
+                    }
+                }
+                std::stable_sort(order.begin(), order.end(),
+                                 [](const std::pair<int64_t, int64_t>& x,
+                                    const std::pair<int64_t, int64_t>& y) { return x.first > y.first; });
+                p.items.resize(2 * order.size());
+                for (size_t n = 0; n < order.size(); ++n) {
+                    p.items[2 * n] = raw[2 * order[n].second];
+                    p.items[2 * n + 1] = raw[2 * order[n].second + 1];
+                }
+            }
+        } else {
+            p.ws_table_bytes = 0;
+        }
+        if (p.dec_merge) {
+            const size_t rows = size_t(split_slots) * size_t(d.N) * FA_DEC_ROWS;
             p.ws_opart_offset = off;
-            off = align256(off + slots * size_t(d.D) * sizeof(float));
+            off = align256(off + rows * size_t(d.D) * sizeof(float));
             p.ws_lse_offset = off;
-            off = align256(off + slots * sizeof(float));
+            off = align256(off + rows * sizeof(float));
         }
         p.ws_bytes = p.empty ? 0 : off;
-        p.ws_table_bytes = p.table && !p.empty ? p.ws_items_offset : 0;
     } else if (p.table) {
         p.n_items = p.n_qtiles_total;
         if (with_tables && !sizes_only) {
@@ -440,6 +528,9 @@ void fa_plan_workspace_image(const fa_plan& plan, std::vector<unsigned char>* im
     if (!plan.items.empty())
         std::memcpy(image->data() + plan.ws_items_offset, plan.items.data(),
                     plan.items.size() * sizeof(int32_t));
+    if (!plan.dec_batch.empty())
+        std::memcpy(image->data() + plan.ws_dec_batch_offset, plan.dec_batch.data(),
+                    plan.dec_batch.size() * sizeof(int32_t));
 }
 
 // ---------------------------------------------------------------------------------------

@@ -39,12 +39,19 @@ constexpr int FA_MFMA32_BN = 64;
 constexpr int FA_GEN_BM = 64;
 constexpr int FA_GEN_BN = 16;
 // Split-KV decode (every sequence has at most FA_DEC_ROWS query rows): one workgroup per
-// (batch, head, split), 64-key tiles; splits are sized so the launch has about
-// FA_DEC_TARGET_WGS workgroups and every split at least FA_DEC_MIN_TILES tiles.
+// (batch, kv split, head), 64-key tiles. The planner's launch model, in kv tiles: a workgroup
+// costs its tiles plus FA_DEC_WG_COST (its fixed start-up and combine, measured at about
+// three tiles' time), FA_DEC_SLOTS workgroups run at once with D = 128 (twice that with
+// D = 64: the kernel's LDS allows one or two per CU), the merge kernel costs
+// FA_DEC_MERGE_COST; splits hold at least FA_DEC_MIN_TILES tiles, at most
+// FA_DEC_MAX_SPLITS per sequence.
 constexpr int FA_DEC_ROWS = 16;
 constexpr int FA_DEC_BN = 64;
-constexpr int FA_DEC_TARGET_WGS = 1024;
+constexpr int FA_DEC_WG_COST = 3;
+constexpr int FA_DEC_MERGE_COST = 3;
+constexpr int FA_DEC_SLOTS = 256;
 constexpr int FA_DEC_MIN_TILES = 8;
+constexpr int FA_DEC_MAX_SPLITS = 64;
 // Paged K / V in the ping-pong kernel: pages of a power-of-two size >= 64 (a 64-key tile never
 // straddles two pages) and at most this many pages per sequence.
 constexpr int FA_PP_MAX_PAGES = 2048;
@@ -71,8 +78,14 @@ struct fa_plan {
     size_t ws_bytes = 0;
     size_t ws_table_bytes = 0;  // leading part of the workspace the host uploads (geometry, items)
     size_t ws_items_offset = 0;
-    // Split-KV decode: splits per (batch, head) and the partial (O, LSE) buffers in the workspace.
+    // Split-KV decode. n_items counts (batch, split) entries; fixed-length mode splits every
+    // batch n_split ways (entry e = b * n_split + split), table mode lists the entries in
+    // `items` (longest first) and per batch (first partial slot, splits) in `dec_batch`.
+    // Batches with more than one split write fp32 partial O / LSE for the merge kernel.
     int32_t n_split = 1;
+    bool dec_merge = false;
+    std::vector<int32_t> dec_batch;
+    size_t ws_dec_batch_offset = 0;
     size_t ws_opart_offset = 0, ws_lse_offset = 0;
     // Strides in elements.
     int64_t q_bs = 0, q_hs = 0, q_rs = 0;

@@ -411,14 +411,23 @@ def _align256(x):
 
 def test_decode_plan_split_counts(lib):
     """At most 16 query rows per sequence selects the split-KV decode kernel (kernel 3, tiles
-    of 16 rows x 64 keys). Splits per (batch, head): enough for ~1024 workgroups, at most one
-    per 8 kv tiles; with more than one split the workspace holds the fp32 partial O
-    [B N splits, 16, D] and LSE [B N splits, 16], 256-byte aligned."""
-    for B, N, skv, n_split in [(1, 1, 333, 1), (1, 2, 5000, 9), (2, 32, 8192, 16), (4, 32, 32768, 8),
-                               (64, 32, 32768, 1)]:
+    of 16 rows x 64 keys). The split count comes from the launch model (a workgroup costs its
+    kv tiles + 3, 256 run at once with D = 128, whole rounds when all are equal, a merge costs
+    3, fewer splits win ties within 1%); the values below are worked by hand from that rule.
+    work_items counts (batch, split) entries per head; with splits the workspace holds the
+    fp32 partial O [slots, N, 16, D] and LSE [slots, N, 16], 256-byte aligned."""
+    for B, N, skv, n_split in [
+        (1, 1, 333, 1),        # 6 tiles: below one 8-tile split
+        (1, 2, 5000, 10),      # 79 tiles, 2 pairs: 10 splits of 8 (est 14) beat 9 of 9 (15)
+        (2, 32, 8192, 4),      # 4 x 32 tiles: 256 workgroups in one round (38) beat 8 x 16 (2 rounds, 41)
+        (4, 32, 32768, 2),     # 2 x 256 tiles: one round (262) beats one split (515) and 4 x 128 (265)
+        (8, 32, 8192, 1),      # 256 pairs of 128 tiles: one round, no merge (131)
+        (64, 32, 32768, 1),    # 2048 pairs: no search
+    ]:
         d = fb.make_dims(2, 0, B=B, N=N, Sq=1, Skv=skv, D=128)
         st = fb.fa_plan_stats(d, "BNSD", 3)
         assert (st["kernel"], st["block_m"], st["block_n"]) == (3, 16, 64)
+        assert st["work_items"] == B * n_split, (B, N, skv, st)
         ws = fb.fa_fwd_workspace_size(d, "BNSD", 3)
         slots = B * N * n_split * 16
         assert ws == (0 if n_split == 1 else _align256(slots * 128 * 4) + _align256(slots * 4)), (B, N, skv)
@@ -428,11 +437,18 @@ def test_decode_plan_split_counts(lib):
     assert fb.fa_plan_stats(fb.make_dims(2, 0, B=1, N=1, Sq=1, Skv=64, D=96), "BNSD", 3)["kernel"] == 0
     assert fb.fa_plan_stats(fb.make_dims(2, 0, B=1, N=1, Sq=1, Skv=64, D=128), "BNSD", 1,
                             has_mask=True)["kernel"] == 1
-    # TND: the per-batch geometry table comes first
+    # TND: per-batch splits. Batch 0 (141 tiles) takes 18 splits of 8 tiles; batches 1 (no
+    # rows) and 2 (no keys) one entry each and no partial slots. Workspace: geometry (3 x 32
+    # bytes), 20 (batch, split) entries, 3 (first slot, splits) pairs, then 18 x 2 slots.
     d = tnd([1, 0, 16], [9000, 5, 0])
-    ws = fb.fa_fwd_workspace_size(d, "TND", 3, [1, 1, 17], [9000, 9005, 9005])
-    n_split = max(1, min(-(-1024 // (3 * 2)), -(-9000 // 64) // 8))
-    assert ws == _align256(3 * 32) + _align256(3 * 2 * n_split * 16 * 128 * 4) + _align256(3 * 2 * n_split * 16 * 4)
+    qc, kc = [1, 1, 17], [9000, 9005, 9005]
+    st = fb.fa_plan_stats(d, "TND", 3, actual_seq_qlen=qc, actual_seq_kvlen=kc)
+    assert st["kernel"] == 3 and st["work_items"] == 20, st
+    ws = fb.fa_fwd_workspace_size(d, "TND", 3, qc, kc)
+    tables = _align256(_align256(_align256(3 * 32) + 20 * 8) + 3 * 8)
+    slots = 18 * 2 * 16
+    assert ws == tables + _align256(slots * 128 * 4) + _align256(slots * 4)
+    assert st["workspace_bytes"] == ws
 
 
 # ---------------------------------------------------------------------------------------
