@@ -932,23 +932,47 @@ fa_fwd_pp(const fa_kargs a) {
 
     // Epilogue: O = O / l, LSE = ln2 (m + log2 l); rows with nothing visible give 0 and -inf.
     const float l_tot = pair_sum(l_run);
-    if (row_ok) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (hl == 0) {
-            a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + row] =
-                l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-        }
-        uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.q_bs + h * a.q_hs +
-                       (int64_t(g.q_start) + row) * a.q_rs;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (row_ok && hl == 0) {
+        a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + row] =
+            l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    // O goes out as whole rows: each wave stages its 32 x D tile (bf16 / fp16) in half of one
+    // K or V buffer and reads it back one row per KCH lanes, so every store instruction writes
+    // 64 / KCH complete rows. A lane's accumulators hold one query row and 4-element runs of
+    // columns, which stored directly would give row-strided 8-byte pieces. Group A runs this
+    // while group B's last matrix phase reads set S = (n_tiles - 1) % 4 and the last (empty)
+    // tile loads fill set S + 3, so A takes set S + 1, whose loads landed phases ago; group B
+    // runs it after its final wait, when every load and read is done, and takes set S + 2.
+    // Rows are KCH 16-byte chunks, chunk c of row r stored at c ^ (r % KCH).
+    {
+        const int set = (((n_tiles - 1) & 3) + 1 + grp) & 3;
+        u32x4* kset = set == 0 ? lds_k0 : (set == 1 ? lds_k1 : (set == 2 ? lds_k2 : lds_k3));
+        u32x4* vset = set == 0 ? lds_v0 : (set == 1 ? lds_v1 : (set == 2 ? lds_v2 : lds_v3));
+        char* stage = reinterpret_cast<char*>(((wave_u & 2) ? vset : kset) + (wave_u & 1) * (TILE_CHUNKS / 2));
+        constexpr int ROWB = KCH * 16;   // bytes of a staged row
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi) {
-                const int d = 32 * db + 8 * gi + 4 * hl;
+                const int c = 4 * db + gi;   // chunk of columns 32 db + 8 gi .. + 7; this lane has half hl
                 const u32x2 w = {io::pack(oacc[db][4 * gi + 0] * inv, oacc[db][4 * gi + 1] * inv),
                                  io::pack(oacc[db][4 * gi + 2] * inv, oacc[db][4 * gi + 3] * inv)};
-                *reinterpret_cast<u32x2*>(op + d) = w;
+                *reinterpret_cast<u32x2*>(stage + ln * ROWB + (c ^ (ln & (KCH - 1))) * 16 + 8 * hl) = w;
             }
+        }
+        // LDS operations of one wave complete in order; this keeps the compiler from moving the
+        // reads above the writes (other lanes' data).
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        uint16_t* obase = static_cast<uint16_t*>(a.o) + b * a.q_bs + h * a.q_hs + (int64_t(g.q_start) + wrow0) * a.q_rs;
+        constexpr int RPI = 64 / KCH;   // rows per read / store instruction
+        const int c = lane % KCH;
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int r = it * RPI + lane / KCH;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * ROWB + (c ^ (r & (KCH - 1))) * 16);
+            if (wrow0 + r < g.sq) *reinterpret_cast<u32x4*>(obase + int64_t(r) * q_rs + 8 * c) = x;
         }
     }
     // Group A ran one phase ahead: its last barrier matches B's final MM phase.
