@@ -284,12 +284,20 @@ __global__ __launch_bounds__(GB_ROWS) void fa_bwd_dkdv_generic(const fa_bwd_args
 // ------------------------------------------------------------------------------------------
 
 // LDS tiles are 64 rows x D, row-major in 16-byte chunks; chunk c of row r sits at c ^ swz(r).
-// The A-operand reads touch rows 8 (n / 4) + n % 4 (+ const) for n = 0..15 at one chunk: swz
-// maps those 16 rows to distinct values for D = 128 (bits 0-1 and 3-4 of r).
+// Two read patterns must both spread over the banks: A-operand reads (16 bytes per lane; the
+// 16 lanes of a group read rows 8 (n / 4) + n % 4 (+ const) at one logical chunk) and transpose
+// reads (8 bytes per lane; four consecutive rows at logical chunks 2 db and 2 db + 1 per group).
+// D = 128: bits 0-1 of r XOR chunk bits 2-3 and bits 2-3 of r XOR chunk bits 0-1. With
+// SQ_LDS_BANK_CONFLICT, a read loop of each pattern measured no conflict cycles this way; an
+// XOR of chunk bits 0-1 with r bits 0-1 (and 2-3 with r bits 3-4) gave two-way conflicts on
+// the transpose reads. D = 64 (two 128-byte rows per 256 bytes): the same on y = r / 2.
 template <int KCH>
 __device__ __forceinline__ int bw_swz(int r) {
-    if constexpr (KCH == 16) return (r & 3) | (((r >> 3) & 3) << 2);
-    else return (r & 3) | (((r >> 3) & 1) << 2);
+    if constexpr (KCH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else {
+        const int y = r >> 1;
+        return ((y & 1) << 2) | ((y >> 1) & 3);
+    }
 }
 
 // Row (or key) held by value e of a lane in group gq for 16 x 16 block bb of a 64-row tile:
@@ -339,23 +347,76 @@ __device__ __forceinline__ void bw_lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// A operand (16 B) of row `row`, logical chunk c, from a swizzled LDS tile.
+// Per-lane byte offsets, inside a tile, of the two swizzled read patterns, computed once per
+// kernel (bw_swz uses row bits 0-3 only, so rows 32 apart share them):
+//  a[p][kd]: A operand of block bb with bb % 2 = p, row slot n (row bw_perm(bb, n)), logical
+//            chunk 4 kd + gq; block bb adds 32 (bb / 2) rows;
+//  b[hf][db]: transpose read of row 8 gq + 4 hf + n / 4 (+ 32 kk), bytes 32 db + 8 (n % 4).
 template <int D>
-__device__ __forceinline__ u32x4 bw_arow(const u32x4* tile, int row, int c) {
+struct bw_offsets {
+    static constexpr int KCH = D / 8, KD = D / 32, DB = D / 16;
+    int a[2][KD];
+    int b[2][DB];
+    __device__ __forceinline__ bw_offsets(int n, int gq) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int row = bw_perm(p, n);
+#pragma unroll
+            for (int kd = 0; kd < KD; ++kd) a[p][kd] = (row * KCH + ((4 * kd + gq) ^ bw_swz<KCH>(row))) * 16;
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int row = 8 * gq + 4 * hf + (n >> 2);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int byte = 32 * db + 8 * (n & 3);   // within the logical row
+                b[hf][db] = (row * KCH + ((byte >> 4) ^ bw_swz<KCH>(row))) * 16 + (byte & 15);
+            }
+        }
+    }
+};
+
+// A operand (16 B) of block bb, k-step kd, from a swizzled LDS tile.
+template <int D>
+__device__ __forceinline__ u32x4 bw_arow(const u32x4* tile, const bw_offsets<D>& o, int bb, int kd) {
     constexpr int KCH = D / 8;
-    return tile[row * KCH + (c ^ bw_swz<KCH>(row))];
+    const char* p = reinterpret_cast<const char*>(tile) + 32 * (bb >> 1) * KCH * 16 + o.a[bb & 1][kd];
+    return *reinterpret_cast<const u32x4*>(p);
 }
 
 // B operand: rows 32 kk + 8 gq + 0..7 of column 16 db + n, through two transpose reads.
 template <int D>
-__device__ __forceinline__ u32x4 bw_bcol(const u32x4* tile, int kk, int db, int gq, int n) {
+__device__ __forceinline__ u32x4 bw_bcol(const u32x4* tile, const bw_offsets<D>& o, int kk, int db) {
+    constexpr int KCH = D / 8;
+    const char* base = reinterpret_cast<const char*>(tile) + 32 * kk * KCH * 16;
+    u32x4 out;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(base + o.b[hf][db]));
+        out[2 * hf] = __builtin_bit_cast(u32x2, x)[0];
+        out[2 * hf + 1] = __builtin_bit_cast(u32x2, x)[1];
+    }
+    return out;
+}
+
+// The same two reads with the offsets computed at each access (the dK dV kernel: there the
+// offset table costs more registers than the per-access arithmetic saves, measured).
+template <int D>
+__device__ __forceinline__ u32x4 bw_arow_at(const u32x4* tile, int row, int c) {
+    constexpr int KCH = D / 8;
+    return tile[row * KCH + (c ^ bw_swz<KCH>(row))];
+}
+
+template <int D>
+__device__ __forceinline__ u32x4 bw_bcol_at(const u32x4* tile, int kk, int db, int gq, int n) {
     constexpr int KCH = D / 8;
     const char* base = reinterpret_cast<const char*>(tile);
     u32x4 out;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
         const int row = 32 * kk + 8 * gq + 4 * hf + (n >> 2);
-        const int byte = 32 * db + 8 * (n & 3);          // within the logical row
+        const int byte = 32 * db + 8 * (n & 3);
         const int chunk = (byte >> 4) ^ bw_swz<KCH>(row);
         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(base + (row * KCH + chunk) * 16 + (byte & 15)));
@@ -390,6 +451,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
     };
     const int lane = threadIdx.x & 63, wave = fa_uniform(threadIdx.x >> 6);
     const int n = lane & 15, gq = lane >> 4;
+    const bw_offsets<D> lo(n, gq);
     const int nqb = (a.n_qt * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
     const int bh = blockIdx.x / nqb, qb = blockIdx.x % nqb;
     const int b = bh / a.N, h = bh % a.N;
@@ -444,11 +506,10 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
         for (int bb = 0; bb < 4; ++bb) {
             s[bb] = f32x4{};
             dp[bb] = f32x4{};
-            const int key = bw_perm(bb, n);
 #pragma unroll
             for (int kd = 0; kd < KD; ++kd) {
-                s[bb] = mm::mma(bw_arow<D>(kt_, key, 4 * kd + gq), qop[kd], s[bb]);
-                dp[bb] = mm::mma(bw_arow<D>(vt_, key, 4 * kd + gq), dop_[kd], dp[bb]);
+                s[bb] = mm::mma(bw_arow<D>(kt_, lo, bb, kd), qop[kd], s[bb]);
+                dp[bb] = mm::mma(bw_arow<D>(vt_, lo, bb, kd), dop_[kd], dp[bb]);
             }
         }
         const int j0 = kt * BW_T;
@@ -477,7 +538,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) acc[db] = mm::mma(dsop[kk], bw_bcol<D>(kt_, kk, db, gq, n), acc[db]);
+            for (int kk = 0; kk < 2; ++kk) acc[db] = mm::mma(dsop[kk], bw_bcol<D>(kt_, lo, kk, db), acc[db]);
         __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * LPT));   // tile kt + 1 has landed
         bw_lds_barrier();
     };
@@ -603,8 +664,8 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args
             const int row = bw_perm(rb, n);
 #pragma unroll
             for (int kd = 0; kd < KD; ++kd) {
-                s[rb] = mm::mma(bw_arow<D>(qt_, row, 4 * kd + gq), kop[kd], s[rb]);
-                dp[rb] = mm::mma(bw_arow<D>(dt_, row, 4 * kd + gq), vop[kd], dp[rb]);
+                s[rb] = mm::mma(bw_arow_at<D>(qt_, row, 4 * kd + gq), kop[kd], s[rb]);
+                dp[rb] = mm::mma(bw_arow_at<D>(dt_, row, 4 * kd + gq), vop[kd], dp[rb]);
             }
         }
         // Every (row, key) of the 64 rows x this wave's 16 keys visible: no per-element test.
@@ -637,8 +698,8 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                dv[db] = mm::mma(pop[kk], bw_bcol<D>(dt_, kk, db, gq, n), dv[db]);
-                dk[db] = mm::mma(dsop[kk], bw_bcol<D>(qt_, kk, db, gq, n), dk[db]);
+                dv[db] = mm::mma(pop[kk], bw_bcol_at<D>(dt_, kk, db, gq, n), dv[db]);
+                dk[db] = mm::mma(dsop[kk], bw_bcol_at<D>(qt_, kk, db, gq, n), dk[db]);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
