@@ -86,6 +86,23 @@ __device__ __forceinline__ void bw_row_range(const fa_geom& g, int j0, int j1, i
     hi = min(g.sq - 1, j1 - g.a);
 }
 
+// Block w of a launch of pairs x nblk workgroups -> (pair, block). Workgroups go round-robin
+// over the 8 XCDs; when the pair count is a multiple of 8, XCD x takes whole pairs x, x + 8, ...
+// so every XCD gets the same mix of light and heavy blocks (block b otherwise lands on XCD
+// b % 8 for every pair, and under causal masks the work grows with b) and a pair's K / V stay in
+// one L2. reverse: hand out the blocks last first (dQ, whose last blocks see the most keys).
+__device__ __forceinline__ void bw_block(int w, int pairs, int nblk, bool reverse, int& pair, int& blk) {
+    if ((pairs & 7) == 0) {
+        const int x = w & 7, s = w >> 3;
+        pair = (s / nblk) * 8 + x;
+        blk = s % nblk;
+    } else {
+        pair = w / nblk;
+        blk = w % nblk;
+    }
+    if (reverse) blk = nblk - 1 - blk;
+}
+
 // Alibi bias in the log2 domain (AL: 1 linear, right- or left-aligned per aoff; 2 square root).
 template <int AL>
 __device__ __forceinline__ float bw_bias2(float slope2, int i, int j, int off, int aoff) {
@@ -453,7 +470,8 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
     const int n = lane & 15, gq = lane >> 4;
     const bw_offsets<D> lo(n, gq);
     const int nqb = (a.n_qt * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
-    const int bh = blockIdx.x / nqb, qb = blockIdx.x % nqb;
+    int bh, qb;
+    bw_block(blockIdx.x, a.B * a.N, nqb, true, bh, qb);
     const int b = bh / a.N, h = bh % a.N;
     const fa_geom g = bw_geom(a, b);
     const int i0 = qb * BW2_BLOCK;
@@ -588,7 +606,8 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args
     __shared__ __attribute__((aligned(16))) float lds_dl[2][BW_T];
     const int lane = threadIdx.x & 63, wave = fa_uniform(threadIdx.x >> 6);
     const int n = lane & 15, gq = lane >> 4;
-    const int bh = blockIdx.x / a.n_kt, kt = blockIdx.x % a.n_kt;
+    int bh, kt;
+    bw_block(blockIdx.x, a.B * a.N, a.n_kt, false, bh, kt);
     const int b = bh / a.N, h = bh % a.N;
     const fa_geom g = bw_geom(a, b);
     const int j0 = kt * BW_T;
