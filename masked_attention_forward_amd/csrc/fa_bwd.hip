@@ -13,7 +13,7 @@
 // and loops over the kv tiles it sees (dQ). Every output element is written by exactly one
 // workgroup: no atomics, bitwise deterministic.
 //
-//  * MFMA kernels (fp16 / bf16, D in {64, 128}, every mode but the explicit mask): four waves
+//  * MFMA kernels (fp16 / bf16, D in {64, 128}, every mode but the explicit mask): eight waves
 //    own 16 keys (dK dV) or 16 query rows (dQ) each, with 16x16x32 MFMAs. The products whose
 //    contraction runs over rows or keys take their left operand straight from the accumulators
 //    of the preceding product: tile rows are permuted so that a lane's four values of one
@@ -347,13 +347,13 @@ __device__ __forceinline__ void bw_load2(const uint16_t* x, const uint16_t* y, i
     bw_tile_load<D, NT>(y + int64_t(r0) * rs, rs, rows, dy);
 }
 
-// The dQ kernel: eight waves of 16 rows, so one staged kv tile feeds 128 rows; tiles stream
-// through a ring of four LDS buffers, loaded three tiles ahead, each wave waiting (vmcnt) only
-// for the tile the next step reads. The ring buffers are separate arrays picked at compile
-// time, so the compiler sees which buffer every access and load touches. (The same ring for
-// dK dV, with 128 keys per workgroup, ran 5% slower than the double-buffered kernel below.)
+// The MFMA kernels: eight waves of 16 rows (dQ) or 16 keys (dK dV), so one staged tile feeds
+// 128 rows or keys; tiles stream through a ring of four LDS buffers, loaded three tiles ahead,
+// each wave waiting (vmcnt) only for the tile the next step reads. The ring buffers are
+// separate arrays picked at compile time, so the compiler sees which buffer every access and
+// load touches.
 constexpr int BW2_THREADS = 512;
-constexpr int BW2_BLOCK = 128;   // query rows per dQ workgroup
+constexpr int BW2_BLOCK = 128;   // query rows (dQ) or keys (dK dV) per workgroup
 
 // Workgroup barrier that waits for this wave's LDS operations (lgkmcnt 0) but not for its
 // loads into LDS still in flight (vmcnt), which each step waits for explicitly.
@@ -411,32 +411,6 @@ __device__ __forceinline__ u32x4 bw_bcol(const u32x4* tile, const bw_offsets<D>&
     for (int hf = 0; hf < 2; ++hf) {
         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(base + o.b[hf][db]));
-        out[2 * hf] = __builtin_bit_cast(u32x2, x)[0];
-        out[2 * hf + 1] = __builtin_bit_cast(u32x2, x)[1];
-    }
-    return out;
-}
-
-// The same two reads with the offsets computed at each access (the dK dV kernel: there the
-// offset table costs more registers than the per-access arithmetic saves, measured).
-template <int D>
-__device__ __forceinline__ u32x4 bw_arow_at(const u32x4* tile, int row, int c) {
-    constexpr int KCH = D / 8;
-    return tile[row * KCH + (c ^ bw_swz<KCH>(row))];
-}
-
-template <int D>
-__device__ __forceinline__ u32x4 bw_bcol_at(const u32x4* tile, int kk, int db, int gq, int n) {
-    constexpr int KCH = D / 8;
-    const char* base = reinterpret_cast<const char*>(tile);
-    u32x4 out;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-        const int row = 32 * kk + 8 * gq + 4 * hf + (n >> 2);
-        const int byte = 32 * db + 8 * (n & 3);
-        const int chunk = (byte >> 4) ^ bw_swz<KCH>(row);
-        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(base + (row * KCH + chunk) * 16 + (byte & 15)));
         out[2 * hf] = __builtin_bit_cast(u32x2, x)[0];
         out[2 * hf + 1] = __builtin_bit_cast(u32x2, x)[1];
     }
@@ -595,31 +569,67 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
     }
 }
 
-// dK and dV: four waves x 16 keys; q tiles of 64 rows (Q, dO, LSE, Delta) through LDS.
+// dK and dV: eight waves x 16 keys; q tiles of 64 rows (Q, dO, LSE, Delta) through the LDS
+// ring. Wave 0 also loads each tile's LSE and Delta (one 4-byte load per lane each).
 template <int D, bool IS_BF16, int AL>
-__global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args a) {
+__global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args a) {
     using io = mfma_io<IS_BF16>;
     using mm = mfma16_io<IS_BF16>;
     constexpr int KD = D / 32, DB = D / 16, TILE_U4 = BW_T * D / 8;
-    __shared__ u32x4 lds_q[2][TILE_U4], lds_do[2][TILE_U4];
-    __shared__ __attribute__((aligned(16))) float lds_l[2][BW_T];
-    __shared__ __attribute__((aligned(16))) float lds_dl[2][BW_T];
+    constexpr int LPT = 2 * TILE_U4 / BW2_THREADS;   // direct loads per thread and q tile (Q and dO)
+    __shared__ u32x4 q0[TILE_U4], q1[TILE_U4], q2[TILE_U4], q3[TILE_U4];
+    __shared__ u32x4 o0[TILE_U4], o1[TILE_U4], o2[TILE_U4], o3[TILE_U4];
+    __shared__ __attribute__((aligned(16))) float l0[BW_T], l1[BW_T], l2[BW_T], l3[BW_T];
+    __shared__ __attribute__((aligned(16))) float d0[BW_T], d1[BW_T], d2[BW_T], d3[BW_T];
+    auto qbuf = [&](auto s_tag) __attribute__((always_inline)) -> u32x4* {
+        constexpr int S = decltype(s_tag)::value & 3;
+        if constexpr (S == 0) return q0;
+        else if constexpr (S == 1) return q1;
+        else if constexpr (S == 2) return q2;
+        else return q3;
+    };
+    auto obuf = [&](auto s_tag) __attribute__((always_inline)) -> u32x4* {
+        constexpr int S = decltype(s_tag)::value & 3;
+        if constexpr (S == 0) return o0;
+        else if constexpr (S == 1) return o1;
+        else if constexpr (S == 2) return o2;
+        else return o3;
+    };
+    auto lbuf = [&](auto s_tag) __attribute__((always_inline)) -> float* {
+        constexpr int S = decltype(s_tag)::value & 3;
+        if constexpr (S == 0) return l0;
+        else if constexpr (S == 1) return l1;
+        else if constexpr (S == 2) return l2;
+        else return l3;
+    };
+    auto dbuf = [&](auto s_tag) __attribute__((always_inline)) -> float* {
+        constexpr int S = decltype(s_tag)::value & 3;
+        if constexpr (S == 0) return d0;
+        else if constexpr (S == 1) return d1;
+        else if constexpr (S == 2) return d2;
+        else return d3;
+    };
     const int lane = threadIdx.x & 63, wave = fa_uniform(threadIdx.x >> 6);
     const int n = lane & 15, gq = lane >> 4;
-    int bh, kt;
-    bw_block(blockIdx.x, a.B * a.N, a.n_kt, false, bh, kt);
+    const bw_offsets<D> lo(n, gq);
+    const int nkb = (a.n_kt * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
+    int bh, kb;
+    bw_block(blockIdx.x, a.B * a.N, nkb, false, bh, kb);
     const int b = bh / a.N, h = bh % a.N;
     const fa_geom g = bw_geom(a, b);
-    const int j0 = kt * BW_T;
+    const int j0 = kb * BW2_BLOCK;
     if (j0 >= g.skv) return;
     const int q_rs = int(a.q_rs), kv_rs = int(a.kv_rs);
     const int64_t qo = b * a.q_bs + h * a.q_hs + int64_t(g.q_start) * a.q_rs;
     const int64_t ko = b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qo;
     const uint16_t* dop = static_cast<const uint16_t*>(a.dout) + qo;
+    const float* lsep = a.lse + b * a.lse_bs + h * a.lse_hs + g.q_start;
+    const float* dlp = a.delta + b * a.lse_bs + h * a.lse_hs + g.q_start;
 
     // This lane's key (the S column) and its operands.
-    const int j = j0 + 16 * wave + n;
+    const int wkey0 = j0 + 16 * wave;
+    const int j = wkey0 + n;
     u32x4 kop[KD], vop[KD];
     {
         const int bytes = ((g.skv - 1) * kv_rs + D) * 2;
@@ -635,7 +645,7 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args
     const float slope2 = AL ? a.slopes[h] * kLog2e : 0.f;
     const int off = g.skv - g.sq, aoff = a.alibi_left ? 0 : off;
     int r_lo, r_hi;
-    bw_row_range(g, j0, min(j0 + BW_T, g.skv) - 1, r_lo, r_hi);
+    bw_row_range(g, j0, min(j0 + BW2_BLOCK, g.skv) - 1, r_lo, r_hi);
     const int t_begin = r_lo / BW_T, t_end = r_lo <= r_hi ? r_hi / BW_T + 1 : t_begin;
 
     f32x4 dk[DB], dv[DB];
@@ -644,62 +654,52 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args
         dk[db] = f32x4{};
         dv[db] = f32x4{};
     }
-    const int tid = threadIdx.x;
-    // LSE (log2 domain, +inf past the sequence so that P = 0) and Delta of q tile t.
-    auto stats = [&](int t, float& l2, float& dl) {
-        const int r = t * BW_T + tid;
-        const bool ok = tid < BW_T && t < t_end && r < g.sq;
-        const int64_t li = b * a.lse_bs + h * a.lse_hs + g.q_start + (ok ? r : 0);
-        l2 = ok ? a.lse[li] * kLog2e : INFINITY;
-        dl = ok ? a.delta[li] : 0.f;
-    };
-    // q tile t (none past the range: zeros, nothing read) into buffer buf.
-#define BW_LOAD_Q(t, buf) \
-    bw_load2<D, BW_THREADS>(qp, dop, (t) * BW_T, q_rs, (t) < t_end ? min(BW_T, g.sq - (t) * BW_T) : 0, lds_q[buf], lds_do[buf])
-    if (t_begin < t_end) {
-        float l2, dl;
-        stats(t_begin, l2, dl);
-        BW_LOAD_Q(t_begin, 0);
-        if (tid < BW_T) {
-            lds_l[0][tid] = l2;
-            lds_dl[0][tid] = dl;
+    // q tile t (none past the range: zeros, nothing read): Q and dO by every wave; LSE and
+    // Delta (natural log and plain; rows past the sequence read as zeros) by wave 0.
+    auto load = [&](int t, u32x4* dq_, u32x4* ddo, float* dl, float* ddl) __attribute__((always_inline)) {
+        const int rows = t < t_end ? min(BW_T, g.sq - t * BW_T) : 0;
+        bw_load2<D, BW2_THREADS>(qp, dop, t * BW_T, q_rs, rows, dq_, ddo);
+        if (wave == 0) {
+            const __amdgpu_buffer_rsrc_t rl = fa_rsrc(lsep + t * BW_T, rows * 4);
+            const __amdgpu_buffer_rsrc_t rd = fa_rsrc(dlp + t * BW_T, rows * 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void_t*)dl, 4, lane * 4, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void_t*)ddl, 4, lane * 4, 0, 0, 0);
         }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        float l2n, dln;
-        stats(t + 1, l2n, dln);
-        BW_LOAD_Q(t + 1, buf ^ 1);
-        const u32x4* qt_ = lds_q[buf];
-        const u32x4* dt_ = lds_do[buf];
+    };
+    auto step = [&](auto s_tag, int t) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_tag)::value;
+        using s3 = std::integral_constant<int, (S + 3) & 3>;
+        load(t + 3, qbuf(s3{}), obuf(s3{}), lbuf(s3{}), dbuf(s3{}));
+        const u32x4* qt_ = qbuf(s_tag);
+        const u32x4* dt_ = obuf(s_tag);
+        const float* lt_ = lbuf(s_tag);
+        const float* dlt_ = dbuf(s_tag);
         const int i0 = t * BW_T;
         f32x4 s[4], dp[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
             s[rb] = f32x4{};
             dp[rb] = f32x4{};
-            const int row = bw_perm(rb, n);
 #pragma unroll
             for (int kd = 0; kd < KD; ++kd) {
-                s[rb] = mm::mma(bw_arow_at<D>(qt_, row, 4 * kd + gq), kop[kd], s[rb]);
-                dp[rb] = mm::mma(bw_arow_at<D>(dt_, row, 4 * kd + gq), vop[kd], dp[rb]);
+                s[rb] = mm::mma(bw_arow<D>(qt_, lo, rb, kd), kop[kd], s[rb]);
+                dp[rb] = mm::mma(bw_arow<D>(dt_, lo, rb, kd), vop[kd], dp[rb]);
             }
         }
         // Every (row, key) of the 64 rows x this wave's 16 keys visible: no per-element test.
-        const bool full = i0 + BW_T <= g.sq && fa_tile_full(g, i0, i0 + BW_T - 1, j0 + 16 * wave, 16);
+        const bool full = i0 + BW_T <= g.sq && fa_tile_full(g, i0, i0 + BW_T - 1, wkey0, 16);
         float p[16], ds[16];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
             const int r0 = 32 * (rb >> 1) + 8 * gq + 4 * (rb & 1);   // tile rows r0 .. r0 + 3
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_l[buf][r0]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_dl[buf][r0]);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lt_[r0]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dlt_[r0]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = i0 + r0 + e;
-                const bool vis = full || (j < g.skv && j >= fa_row_lo(g, i) && j <= fa_row_hi(g, i));
-                const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - l4[e])
+                const bool vis = full || (i < g.sq && j < g.skv && j >= fa_row_lo(g, i) && j <= fa_row_hi(g, i));
+                const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) -
+                                                              l4[e] * kLog2e)
                                      : 0.f;
                 p[4 * rb + e] = pv;
                 ds[4 * rb + e] = pv * (dp[rb][e] - d4[e]);
@@ -717,24 +717,44 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_args
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                dv[db] = mm::mma(pop[kk], bw_bcol_at<D>(dt_, kk, db, gq, n), dv[db]);
-                dk[db] = mm::mma(dsop[kk], bw_bcol_at<D>(qt_, kk, db, gq, n), dk[db]);
+                dv[db] = mm::mma(pop[kk], bw_bcol<D>(dt_, lo, kk, db), dv[db]);
+                dk[db] = mm::mma(dsop[kk], bw_bcol<D>(qt_, lo, kk, db), dk[db]);
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        if (tid < BW_T) {
-            lds_l[buf ^ 1][tid] = l2n;
-            lds_dl[buf ^ 1][tid] = dln;
+        // q tile t + 1 has landed (wave 0 issues two more loads per tile).
+        if (wave == 0) __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * (LPT + 2)));
+        else __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * LPT));
+        bw_lds_barrier();
+    };
+    if (t_begin < t_end) {
+        using c0 = std::integral_constant<int, 0>;
+        using c1 = std::integral_constant<int, 1>;
+        using c2 = std::integral_constant<int, 2>;
+        using c3 = std::integral_constant<int, 3>;
+        load(t_begin, q0, o0, l0, d0);
+        load(t_begin + 1, q1, o1, l1, d1);
+        load(t_begin + 2, q2, o2, l2, d2);
+        if (wave == 0) __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * (LPT + 2)));   // K, V and tile 0
+        else __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * LPT));
+        bw_lds_barrier();
+        // Trips of four; every path into a step runs the earlier ones.
+        for (int t = t_begin; t < t_end; t += 4) {
+            step(c0{}, t);
+            if (t + 1 >= t_end) break;
+            step(c1{}, t + 1);
+            if (t + 2 >= t_end) break;
+            step(c2{}, t + 2);
+            if (t + 3 >= t_end) break;
+            step(c3{}, t + 3);
         }
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
     }
-#undef BW_LOAD_Q
     // Keys 16 wave + 4 gq + e, columns 16 db + n.
     uint16_t* dkp = static_cast<uint16_t*>(a.dk) + ko;
     uint16_t* dvp = static_cast<uint16_t*>(a.dv) + ko;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int key = j0 + 16 * wave + 4 * gq + e;
+        const int key = wkey0 + 4 * gq + e;
         if (key < g.skv) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -823,7 +843,8 @@ void launch_generic_t(const fa_bwd_args& a, int al, bool dense, int64_t pairs, h
 template <int D, bool BF, int AL>
 void launch_mfma(const fa_bwd_args& a, int64_t pairs, hipStream_t s) {
     const int64_t nqb = (int64_t(a.n_qt) * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
-    if (a.n_kt > 0) fa_bwd_dkdv_mfma<D, BF, AL><<<dim3(unsigned(pairs * a.n_kt)), dim3(BW_THREADS), 0, s>>>(a);
+    const int64_t nkb = (int64_t(a.n_kt) * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
+    if (nkb > 0) fa_bwd_dkdv_mfma<D, BF, AL><<<dim3(unsigned(pairs * nkb)), dim3(BW2_THREADS), 0, s>>>(a);
     if (nqb > 0) fa_bwd_dq_mfma<D, BF, AL><<<dim3(unsigned(pairs * nqb)), dim3(BW2_THREADS), 0, s>>>(a);
 }
 
