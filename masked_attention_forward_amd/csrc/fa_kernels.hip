@@ -1104,12 +1104,29 @@ __global__ __launch_bounds__(DC_THREADS) void fa_decode_split(const fa_kargs a, 
 #pragma unroll
         for (int kd = 0; kd < KD; ++kd) k_off[bb][kd] = (key * kv_rs + 32 * kd + 8 * gq) * 2;
     }
-    const int v_voff = (lane * 16 / ROW_B) * kv_rs * 2 + (lane * 16) % ROW_B;
-    int v_tr[2][2];   // [kk][half]: byte address in the tile of this lane's transpose read (column block 0)
+    // V tile in LDS: rows of D / 8 16-byte chunks; with D = 128, chunk c of row r sits at
+    // c ^ vswz(r), vswz(r) = 4 (r % 4) + (r / 4) % 4, so that the transpose reads (per 16 lanes four
+    // consecutive rows at two chunks) spread over all banks. With SQ_LDS_BANK_CONFLICT the
+    // unswizzled tile spent 86% of its LDS cycles in conflicts; a read loop of this pattern
+    // measured none with this swizzle. D = 64 keeps the plain layout. The swizzle depends on row
+    // bits 0-3 only, so rows 32 apart share it.
+    auto vswz = [](int r) { return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : 0; };
+    int v_voff[4];   // source offset of this lane's 16 bytes in direct load p (by p % 4; + p RPL rows)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int q = 0; q < 4; ++q) {
+        const int r = lane * 16 / ROW_B, c = ((lane * 16) % ROW_B) / 16;
+        v_voff[q] = r * kv_rs * 2 + ((c ^ vswz(q * RPL + r)) * 16);
+    }
+    int v_rd[2][DB];   // [half][column block]: LDS byte offset of this lane's transpose read (+ 32 kk rows)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) v_tr[kk][hf] = (32 * kk + 8 * gq + 4 * hf + (n >> 2)) * ROW_B + 8 * (n & 3);
+    for (int hf = 0; hf < 2; ++hf) {
+        const int r = 8 * gq + 4 * hf + (n >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int byte = 32 * db + 8 * (n & 3);
+            v_rd[hf][db] = r * ROW_B + (((byte >> 4) ^ vswz(r)) * 16) + (byte & 15);
+        }
+    }
 
     u32x4 kreg[2][NK];
     char* const vbuf = reinterpret_cast<char*>(lds_v) + wave * 2 * TILE_U4 * 16;
@@ -1137,7 +1154,7 @@ __global__ __launch_bounds__(DC_THREADS) void fa_decode_split(const fa_kargs a, 
 #pragma unroll
         for (int p = 0; p < NV; ++p)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vbuf + (BUF * TILE_U4 + p * 64) * 16), 16,
-                                                     v_voff + p * RPL * kv_rs * 2, 0, 0, 0);
+                                                     v_voff[p & 3] + p * RPL * kv_rs * 2, 0, 0, 0);
     };
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -1214,9 +1231,9 @@ __global__ __launch_bounds__(DC_THREADS) void fa_decode_split(const fa_kargs a, 
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(vb + v_tr[kk][0] + 32 * db));
+                    (__attribute__((address_space(3))) s16x4*)(vb + 32 * kk * ROW_B + v_rd[0][db]));
                 const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(vb + v_tr[kk][1] + 32 * db));
+                    (__attribute__((address_space(3))) s16x4*)(vb + 32 * kk * ROW_B + v_rd[1][db]));
                 const u32x4 vop = {__builtin_bit_cast(u32x2, x0)[0], __builtin_bit_cast(u32x2, x0)[1],
                                    __builtin_bit_cast(u32x2, x1)[0], __builtin_bit_cast(u32x2, x1)[1]};
                 oacc[db] = mm::mma(pop[kk], vop, oacc[db]);
