@@ -21,6 +21,10 @@
 //    one exchange with lane^32, and P^T is taken straight from the S^T accumulators. K and V
 //    tiles go from HBM straight into XOR-swizzled LDS with buffer loads; the V^T operand is
 //    read with ds_read_b64_tr_b16 transpose reads.
+//  * fa_decode_split + fa_decode_merge (every sequence has at most 16 query rows): each
+//    workgroup takes one (batch, kv split, head); 16x16x32 MFMAs with the query rows as the 16
+//    columns, K straight from HBM into registers, V through swizzled per-wave LDS buffers; the
+//    merge combines the splits' (O, LSE). The planner sizes the splits from a launch model.
 //  * fa_fwd_generic: any dtype (fp32 included), D <= 128. One thread per query row, fp32
 //    throughout (P is never rounded), K/V tiles of 16 keys staged in LDS.
 // All visit only kv tiles that hold a visible entry (fa_tile_kv_range) and skip per-element
@@ -126,14 +130,6 @@ __device__ __forceinline__ void fa_decode_item(const fa_kargs& a, int& b, int& h
 // ------------------------------------------------------------------------------------------
 // MFMA kernel
 // ------------------------------------------------------------------------------------------
-
-// LDS index (in 16-byte chunks) of chunk c of row r, for rows of 16 chunks (256 bytes).
-__device__ __forceinline__ int lds_idx16(int r, int c) { return r * 16 + (c ^ (r & 15)); }
-// Same for rows of 8 chunks (128 bytes): two rows share a 256-byte line.
-__device__ __forceinline__ int lds_idx8(int r, int c) {
-    const int line = r >> 1;
-    return line * 16 + ((8 * (r & 1) + c) ^ (line & 7));
-}
 
 // max / sum of x over the lane pair (l, l ^ 32); both lanes get the same bits.
 __device__ __forceinline__ float pair_max(float x) {
