@@ -675,13 +675,17 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
         const float* lt_ = lbuf(s_tag);
         const float* dlt_ = dbuf(s_tag);
         const int i0 = t * BW_T;
+        // k-step outer: consecutive MFMAs go to different accumulators, so none waits on the last.
         f32x4 s[4], dp[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
             s[rb] = f32x4{};
             dp[rb] = f32x4{};
+        }
 #pragma unroll
-            for (int kd = 0; kd < KD; ++kd) {
+        for (int kd = 0; kd < KD; ++kd) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
                 s[rb] = mm::mma(bw_arow<D>(qt_, lo, rb, kd), kop[kd], s[rb]);
                 dp[rb] = mm::mma(bw_arow<D>(dt_, lo, rb, kd), vop[kd], dp[rb]);
             }
@@ -714,9 +718,9 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
             dsop[kk] = u32x4{io::pack(dl[0], dl[1]), io::pack(dl[2], dl[3]), io::pack(dl[4], dl[5]), io::pack(dl[6], dl[7])};
         }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
+            for (int db = 0; db < DB; ++db) {
                 dv[db] = mm::mma(pop[kk], bw_bcol<D>(dt_, lo, kk, db), dv[db]);
                 dk[db] = mm::mma(dsop[kk], bw_bcol<D>(qt_, lo, kk, db), dk[db]);
             }
