@@ -1,6 +1,7 @@
 """Benchmark: masked attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold]
+                    [--prewarm-ms MS]
 
 One step is one fa_fwd call (fa_fwd_paged with --block-size) over the whole workload (inputs
 already resident in HBM). The metric is effective TFLOP/s: 4 * D flops per visible (query,
@@ -10,7 +11,9 @@ pair count comes from the library's mask probe (checked bit-exactly against the 
 the test suite) and is cross-checked against a closed form where one exists.
 
 Prints one JSON line. Timing uses HIP events recorded on the stream fa_fwd is launched on
-(torch's current stream). The CPU baseline times the fp64 oracle on a bounded sample of
+(torch's current stream). Before the counted warm-up steps, untimed steps run for --prewarm-ms
+of wall time (default 500): the GPU raises its clock over the first tens of milliseconds of load,
+so without them a short timed region measures the ramp rather than the sustained rate. The CPU baseline times the fp64 oracle on a bounded sample of
 the same workload (a few whole heads) on this host's cores.
 """
 
@@ -54,6 +57,32 @@ def kernel_sources_sha(sources=None) -> str:
                 if t and not t.startswith(b"//"):
                     h.update(t + b"\n")
     return h.hexdigest()[:16]
+
+
+def prewarm(step, ms_target: float) -> int:
+    """Untimed steps for about `ms_target` ms of wall time, before the counted warm-up steps.
+
+    After idle the GPU raises its clock over the first tens of milliseconds of load: measured on
+    the causal 8192 prefill, launches in the first 40 ms after a 1 s pause ran 7% slower than from
+    80 ms on, where the rate then held for seconds. A few counted warm-up steps of a short workload
+    end inside that ramp, so the timed steps would measure it rather than the sustained rate.
+    Steps go out in chunks of about 20 ms with a synchronize after each. Returns the step count."""
+    import torch
+
+    if ms_target <= 0:
+        return 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    chunk = max(1, int(20.0 / max((time.perf_counter() - t0) * 1e3, 1e-3)))
+    n = 1
+    while (time.perf_counter() - t0) * 1e3 < ms_target:
+        for _ in range(chunk):
+            step()
+        torch.cuda.synchronize()
+        n += chunk
+    return n
 
 
 def recorded_traffic(workload: str, path=None, sources=None, kernel=DOMINANT_KERNEL):
@@ -203,6 +232,7 @@ def bench_bwd(args, dev):
 
     pairs = visible_pairs(w, dev)
     flops = 10 * w.D * pairs
+    n_pre = prewarm(step, args.prewarm_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -220,6 +250,7 @@ def bench_bwd(args, dev):
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f16": "f16", "f32": "f32"}[w.dtype], "data": "synthetic (seeded N(0,1) q/k/v/dO)",
+        "timing": {"cache": "warm", "prewarm_ms": args.prewarm_ms, "prewarm_steps": n_pre},
         "config": {"workload": args.workload, "layout": w.layout, "sparse_mode": w.sparse_mode, "B": w.B, "N": w.N,
                    "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "visible_pairs": pairs, "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -240,6 +271,7 @@ def bench_scatter(args, dev):
     kc = torch.zeros(nb, bs, N, D, dtype=torch.bfloat16, device=dev)
     vc = torch.zeros_like(kc)
     slots = torch.randperm(nb * bs, generator=g)[:T].to(torch.int64).to(dev)
+    n_pre = prewarm(lambda: fb.fa_scatter_kv_cache(key, kc, slots, val, vc), args.prewarm_ms)
     for _ in range(args.warmup):
         fb.fa_scatter_kv_cache(key, kc, slots, val, vc)
     torch.cuda.synchronize()
@@ -258,6 +290,7 @@ def bench_scatter(args, dev):
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) keys/values, random distinct slots)",
+        "timing": {"cache": "warm", "prewarm_ms": args.prewarm_ms, "prewarm_steps": n_pre},
         "config": {"workload": "kv_scatter_prefill", "num_tokens": T, "N": N, "D": D, "num_blocks": nb,
                    "block_size": bs, "layout": "Norm"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -286,6 +319,12 @@ def main():
                     help="> 0: read K / V through fa_fwd_paged from caches of pages of this many keys")
     ap.add_argument("--cache-layout", default="Norm", choices=["Norm", "NHSD"],
                     help="paged cache layout (with --block-size)")
+    ap.add_argument("--prewarm-ms", type=float, default=500.0,
+                    help="untimed steps for this many ms of wall time before the warm-up steps "
+                         "(the GPU clock ramps up over the first tens of ms of load; 0: none)")
+    ap.add_argument("--cold", action="store_true",
+                    help="cold caches: read a 512 MiB buffer before every timed launch (more than "
+                         "L2 and the 256 MB Infinity Cache) and time each launch alone with HIP events")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(reference for the HBM byte counters)")
@@ -350,18 +389,42 @@ def main():
     rows_kv = k.numel() // w.D
     alg_bytes = (2 * rows_q * w.D + 2 * rows_kv * w.D) * elem + 4 * rows_q
 
+    n_pre = prewarm(step, args.prewarm_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    timing = {"cache": "warm"}
+    if args.cold:
+        # A read, not a write, evicts the inputs: written lines would leave up to 256 MB dirty in the
+        # caches, and their write-back would fall inside the next timed launch. The read runs on the
+        # same stream before each launch's first event, outside its timed span.
+        flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        sums = []
+        torch.cuda.synchronize()
+        for a0, a1 in evs:
+            sums.append(flush.sum())
+            a0.record(stream)
+            step()
+            a1.record(stream)
+        torch.cuda.synchronize()
+        assert all(int(x) == flush.numel() for x in sums)
+        per = sorted(a0.elapsed_time(a1) for a0, a1 in evs)
+        ms = sum(per) / len(per)
+        timing = {"cache": "cold (512 MiB read before each launch; launches timed one by one)",
+                  "ms_median": round(per[len(per) // 2], 4), "ms_min": round(per[0], 4)}
+    else:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+    timing.update(prewarm_ms=args.prewarm_ms, prewarm_steps=n_pre)
     tflops = flops / (ms * 1e-3) / 1e12
     # At most 16 query rows per sequence: the split-KV decode path, bound by HBM.
     decode = max(w.qlens) <= 16 if w.layout == "TND" else w.Sq <= 16
@@ -382,6 +445,7 @@ def main():
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f16": "f16", "f32": "f32"}[w.dtype],
         "data": "synthetic (seeded N(0,1) q/k/v)",
+        "timing": timing,
         "config": {"workload": args.workload, "layout": w.layout, "sparse_mode": w.sparse_mode,
                    "B": w.B, "N": w.N, "Sq": w.Sq, "Skv": w.Skv, "D": w.D,
                    "pre_tokens": w.pre_tokens, "next_tokens": w.next_tokens,
