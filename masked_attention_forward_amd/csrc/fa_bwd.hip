@@ -675,56 +675,65 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
         const float* lt_ = lbuf(s_tag);
         const float* dlt_ = dbuf(s_tag);
         const int i0 = t * BW_T;
-        // k-step outer: consecutive MFMAs go to different accumulators, so none waits on the last.
+        // Two halves of the tile's 64 rows (blocks 2 hf, 2 hf + 1). Within a half the k-step loop is
+        // outer, so consecutive MFMAs go to different accumulators; across halves the VALU work of
+        // one half can run under the MFMAs of the other.
         f32x4 s[4], dp[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            s[rb] = f32x4{};
-            dp[rb] = f32x4{};
-        }
-#pragma unroll
-        for (int kd = 0; kd < KD; ++kd) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                s[rb] = mm::mma(bw_arow<D>(qt_, lo, rb, kd), kop[kd], s[rb]);
-                dp[rb] = mm::mma(bw_arow<D>(dt_, lo, rb, kd), vop[kd], dp[rb]);
-            }
-        }
         // Every (row, key) of the 64 rows x this wave's 16 keys visible: no per-element test.
         const bool full = i0 + BW_T <= g.sq && fa_tile_full(g, i0, i0 + BW_T - 1, wkey0, 16);
-        float p[16], ds[16];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int r0 = 32 * (rb >> 1) + 8 * gq + 4 * (rb & 1);   // tile rows r0 .. r0 + 3
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lt_[r0]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dlt_[r0]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = i0 + r0 + e;
-                const bool vis = full || (i < g.sq && j < g.skv && j >= fa_row_lo(g, i) && j <= fa_row_hi(g, i));
-                const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) -
-                                                              l4[e] * kLog2e)
-                                     : 0.f;
-                p[4 * rb + e] = pv;
-                ds[4 * rb + e] = pv * (dp[rb][e] - d4[e]);
-            }
-        }
         u32x4 pop[2], dsop[2];
+        auto sdp = [&](int hf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const float* pl = p + 8 * kk;
-            const float* dl = ds + 8 * kk;
-            pop[kk] = u32x4{io::pack(pl[0], pl[1]), io::pack(pl[2], pl[3]), io::pack(pl[4], pl[5]), io::pack(pl[6], pl[7])};
-            dsop[kk] = u32x4{io::pack(dl[0], dl[1]), io::pack(dl[2], dl[3]), io::pack(dl[4], dl[5]), io::pack(dl[6], dl[7])};
-        }
+            for (int r2 = 0; r2 < 2; ++r2) {
+                s[2 * hf + r2] = f32x4{};
+                dp[2 * hf + r2] = f32x4{};
+            }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+            for (int kd = 0; kd < KD; ++kd) {
+#pragma unroll
+                for (int r2 = 0; r2 < 2; ++r2) {
+                    const int rb = 2 * hf + r2;
+                    s[rb] = mm::mma(bw_arow<D>(qt_, lo, rb, kd), kop[kd], s[rb]);
+                    dp[rb] = mm::mma(bw_arow<D>(dt_, lo, rb, kd), vop[kd], dp[rb]);
+                }
+            }
+        };
+        // P and dS of the half's 32 rows x this lane's key, packed as the dV / dK left operands.
+        auto soft = [&](int hf) __attribute__((always_inline)) {
+            float p[8], ds[8];
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const int rb = 2 * hf + r2;
+                const int r0 = 32 * (rb >> 1) + 8 * gq + 4 * (rb & 1);   // tile rows r0 .. r0 + 3
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lt_[r0]);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dlt_[r0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = i0 + r0 + e;
+                    const bool vis = full || (i < g.sq && j < g.skv && j >= fa_row_lo(g, i) && j <= fa_row_hi(g, i));
+                    const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) -
+                                                                  l4[e] * kLog2e)
+                                         : 0.f;
+                    p[4 * r2 + e] = pv;
+                    ds[4 * r2 + e] = pv * (dp[rb][e] - d4[e]);
+                }
+            }
+            pop[hf] = u32x4{io::pack(p[0], p[1]), io::pack(p[2], p[3]), io::pack(p[4], p[5]), io::pack(p[6], p[7])};
+            dsop[hf] = u32x4{io::pack(ds[0], ds[1]), io::pack(ds[2], ds[3]), io::pack(ds[4], ds[5]), io::pack(ds[6], ds[7])};
+        };
+        auto dvdk = [&](int kk) __attribute__((always_inline)) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 dv[db] = mm::mma(pop[kk], bw_bcol<D>(dt_, lo, kk, db), dv[db]);
                 dk[db] = mm::mma(dsop[kk], bw_bcol<D>(qt_, lo, kk, db), dk[db]);
             }
-        }
+        };
+        sdp(0);
+        soft(0);
+        sdp(1);
+        dvdk(0);
+        soft(1);
+        dvdk(1);
         // q tile t + 1 has landed (wave 0 issues two more loads per tile).
         if (wave == 0) __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * (LPT + 2)));
         else __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * LPT));
