@@ -556,7 +556,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
         }
         __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
     }
-    // Rows 16 wave + 4 gq + e, columns 16 db + n.
+    // Rows 16 wave + 4 gq + e, columns 16 db + n. Non-temporal: the kernel never reads dQ back.
     uint16_t* out = static_cast<uint16_t*>(a.dq) + qo;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
         if (r < g.sq) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                out[int64_t(r) * q_rs + 16 * db + n] = uint16_t(io::pack(acc[db][e] * a.scale, 0.f) & 0xffffu);
+                __builtin_nontemporal_store(uint16_t(io::pack(acc[db][e] * a.scale, 0.f) & 0xffffu), &out[int64_t(r) * q_rs + 16 * db + n]);
         }
     }
 }
@@ -762,7 +762,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
         }
         __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
     }
-    // Keys 16 wave + 4 gq + e, columns 16 db + n.
+    // Keys 16 wave + 4 gq + e, columns 16 db + n. Non-temporal: the kernel never reads dK / dV back.
     uint16_t* dkp = static_cast<uint16_t*>(a.dk) + ko;
     uint16_t* dvp = static_cast<uint16_t*>(a.dv) + ko;
 #pragma unroll
@@ -771,8 +771,8 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
         if (key < g.skv) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                dkp[int64_t(key) * kv_rs + 16 * db + n] = uint16_t(io::pack(dk[db][e] * a.scale, 0.f) & 0xffffu);
-                dvp[int64_t(key) * kv_rs + 16 * db + n] = uint16_t(io::pack(dv[db][e], 0.f) & 0xffffu);
+                __builtin_nontemporal_store(uint16_t(io::pack(dk[db][e] * a.scale, 0.f) & 0xffffu), &dkp[int64_t(key) * kv_rs + 16 * db + n]);
+                __builtin_nontemporal_store(uint16_t(io::pack(dv[db][e], 0.f) & 0xffffu), &dvp[int64_t(key) * kv_rs + 16 * db + n]);
             }
         }
     }

@@ -968,7 +968,8 @@ fa_fwd_pp(const fa_kargs a) {
         for (int it = 0; it < 32 / RPI; ++it) {
             const int r = it * RPI + lane / KCH;
             const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * ROWB + (c ^ (r & (KCH - 1))) * 16);
-            if (wrow0 + r < g.sq) *reinterpret_cast<u32x4*>(obase + int64_t(r) * q_rs + 8 * c) = x;
+            // Non-temporal: O is not read again here, so it need not displace K / V in the caches.
+            if (wrow0 + r < g.sq) __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(obase + int64_t(r) * q_rs + 8 * c));
         }
     }
     // Group A ran one phase ahead: its last barrier matches B's final MM phase.
