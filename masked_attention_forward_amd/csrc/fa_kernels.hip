@@ -1148,10 +1148,13 @@ __global__ __launch_bounds__(DC_THREADS) void fa_decode_split(const fa_kargs a, 
         for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
             for (int kd = 0; kd < KD; ++kd) kreg[BUF][bb * KD + kd] = fa_bload(rk, k_off[bb][kd]);
+        // V goes to LDS with the non-temporal hint (aux 2): decode reads each V row once, and the
+        // hint measured 8-13% faster on every decode shape. The same hint on the K loads into
+        // registers was slower.
 #pragma unroll
         for (int p = 0; p < NV; ++p)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vbuf + (BUF * TILE_U4 + p * 64) * 16), 16,
-                                                     v_voff[p & 3] + p * RPL * kv_rs * 2, 0, 0, 0);
+                                                     v_voff[p & 3] + p * RPL * kv_rs * 2, 0, 0, 2);
     };
 
     float m_run = -INFINITY, l_run = 0.f;

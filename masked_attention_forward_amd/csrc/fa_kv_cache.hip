@@ -78,8 +78,9 @@ __global__ __launch_bounds__(256) void fa_kv_scatter(const kv_scatter_args a) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
             const int c = base + u * blockDim.x;
-            if (c < ktot) kx[u] = reinterpret_cast<const T*>(ksrc)[c];
-            if (c < vtot) vx[u] = reinterpret_cast<const T*>(vsrc)[c];
+            // Each source byte is read once: non-temporal, like the stores below.
+            if (c < ktot) kx[u] = __builtin_nontemporal_load(reinterpret_cast<const T*>(ksrc) + c);
+            if (c < vtot) vx[u] = __builtin_nontemporal_load(reinterpret_cast<const T*>(vsrc) + c);
         }
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
