@@ -143,6 +143,45 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_delta(const fa_bwd_args a) 
     if (lane == 0) a.delta[b * a.lse_bs + h * a.lse_hs + g.q_start + i] = s;
 }
 
+// bf16 / fp16 with D % 8 == 0 and 16-byte aligned rows: 16 lanes per row, 16 bytes per lane and
+// load, four rows per wave. O is read only here (non-temporal); dO stays cached for the two
+// kernels after this one.
+constexpr int DLV_ROWS = (BW_THREADS / 64) * 4;   // rows per workgroup of fa_bwd_delta_v
+
+template <typename T>
+__device__ __forceinline__ float half_f(uint32_t bits) {
+    return to_f(__builtin_bit_cast(T, uint16_t(bits)));
+}
+
+template <typename T>
+__global__ __launch_bounds__(BW_THREADS) void fa_bwd_delta_v(const fa_bwd_args a) {
+    const int nrb = (a.n_qt * BW_T + DLV_ROWS - 1) / DLV_ROWS;
+    const int bh = blockIdx.x / nrb;
+    const int b = bh / a.N, h = bh % a.N;
+    const fa_geom g = bw_geom(a, b);
+    const int lane = threadIdx.x & 63, c = lane & 15;
+    const int i = (blockIdx.x % nrb) * DLV_ROWS + (threadIdx.x >> 6) * 4 + (lane >> 4);
+    float s = 0.f;
+    if (i < g.sq) {
+        const int64_t ro = b * a.q_bs + h * a.q_hs + (int64_t(g.q_start) + i) * a.q_rs;
+        const u32x4* op = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.o) + ro);
+        const u32x4* dp = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + ro);
+        for (int k = c; k < a.D / 8; k += 16) {
+            const u32x4 x = __builtin_nontemporal_load(op + k);
+            const u32x4 y = dp[k];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                s = fmaf(half_f<T>(x[w] & 0xffffu), half_f<T>(y[w] & 0xffffu), s);
+                s = fmaf(half_f<T>(x[w] >> 16), half_f<T>(y[w] >> 16), s);
+            }
+        }
+    }
+    // Every lane takes part in the reduction over its 16-lane row group.
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if (c == 0 && i < g.sq) a.delta[b * a.lse_bs + h * a.lse_hs + g.q_start + i] = s;
+}
+
 // ------------------------------------------------------------------------------------------
 // Generic kernels (fp32 arithmetic).
 // ------------------------------------------------------------------------------------------
@@ -967,7 +1006,16 @@ extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const v
     const int al = alibi_slopes == nullptr ? 0 : (alibi_mode == FA_ALIBI_SQRT ? 2 : 1);
     const bool dense = sparse_mode == 1;
     const int32_t dtype = dims->dtype;
-    if (bp.n_qt > 0) {
+    // The vector Delta kernel reads rows as 16-byte chunks: every row offset and both bases must be
+    // 16-byte aligned.
+    const bool delta_v = dtype != FA_DTYPE_F32 && p.D % 8 == 0 && p.q_bs % 8 == 0 && p.q_hs % 8 == 0 &&
+                         p.q_rs % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(dout) & 15) == 0;
+    if (bp.n_qt > 0 && delta_v) {
+        const dim3 grid(unsigned(pairs * ((bp.n_qt * BW_T + DLV_ROWS - 1) / DLV_ROWS)));
+        if (dtype == FA_DTYPE_F16) fa_bwd_delta_v<_Float16><<<grid, dim3(BW_THREADS), 0, s>>>(a);
+        else fa_bwd_delta_v<__bf16><<<grid, dim3(BW_THREADS), 0, s>>>(a);
+    } else if (bp.n_qt > 0) {
         const dim3 grid(unsigned(pairs * ((bp.n_qt * BW_T + DL_ROWS - 1) / DL_ROWS)));
         switch (dtype) {
             case FA_DTYPE_F32: fa_bwd_delta<float><<<grid, dim3(BW_THREADS), 0, s>>>(a); break;

@@ -46,7 +46,7 @@ def check_grad(got, ref, dtype, what):
 
 
 def bwd_case(dev, layout, dtype, D, mode, sq, skv, *, B=2, N=3, qlens=None, kvlens=None, slopes=None,
-             alibi_mode="right", mask=None, mask_bcast=None, seed=0, **kw):
+             alibi_mode="right", mask=None, mask_bcast=None, seed=0, misalign_out=False, **kw):
     if layout == "TND":
         B = len(qlens)
         kw.update(actual_seq_qlen=synth.cumulative_ends(qlens), actual_seq_kvlen=synth.cumulative_ends(kvlens))
@@ -60,6 +60,13 @@ def bwd_case(dev, layout, dtype, D, mode, sq, skv, *, B=2, N=3, qlens=None, kvle
     qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
     out, lse = fb.flash_attention(qd, kd, vd, layout=layout, sparse_mode=mode, scale=scale, alibi_slopes=sl,
                                   alibi_mode=alibi_mode, atten_mask=md, mask_bcast=mask_bcast, **kw)
+    if misalign_out:
+        # The same O, one element past a 16-byte boundary.
+        buf = torch.empty(out.numel() + 1, dtype=out.dtype, device=dev)
+        moved = buf[1:].view(out.shape)
+        moved.copy_(out)
+        out = moved
+        assert out.data_ptr() % 16 != 0
     dq, dk, dv = fb.flash_attention_backward(qd, kd, vd, out, lse, dod, layout=layout, sparse_mode=mode, scale=scale,
                                              alibi_slopes=sl, alibi_mode=alibi_mode, atten_mask=md,
                                              mask_bcast=mask_bcast, **kw)
@@ -96,6 +103,15 @@ def test_bwd_alibi(gpu_device, alibi_mode):
         for mode, args in [(3, {}), (4, dict(pre_tokens=60, next_tokens=7)), (5, dict(prefix=[200, 10]))]:
             bwd_case(gpu_device, layout, dtype, D, mode, 260, 300, slopes=[0.6, 0.25, 0.05], alibi_mode=alibi_mode,
                      seed=900 + D + mode, **args)
+
+
+def test_bwd_delta_paths(gpu_device):
+    """Delta = rowsum(dO * O) has a 16-byte vector kernel for fp16 / bf16 and a scalar one for the
+    rest. Two-byte cases that take the scalar kernel: D not a multiple of 8 (bf16 D 36), and an O
+    whose base is not 16-byte aligned (bf16 D 128, fp16 D 64)."""
+    bwd_case(gpu_device, "BNSD", "bf16", 36, 3, 130, 150, seed=81)
+    bwd_case(gpu_device, "BNSD", "bf16", 128, 3, 130, 150, seed=82, misalign_out=True)
+    bwd_case(gpu_device, "BSND", "f16", 64, 4, 200, 180, seed=83, misalign_out=True, pre_tokens=50, next_tokens=10)
 
 
 def test_bwd_dense_mask(gpu_device):
