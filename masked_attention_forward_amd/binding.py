@@ -164,6 +164,50 @@ def _check_device_tensor(name, t, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _kv_shape_of(q, layout, skv_or_tkv):
+    """The shape k and v must have, given q in `layout` and the key count (Skv, or T_kv for TND)."""
+    lay = _layout_code(layout)
+    if lay == 0:
+        B, N, _, D = q.shape
+        return (B, N, skv_or_tkv, D)
+    if lay == 1:
+        B, _, N, D = q.shape
+        return (B, skv_or_tkv, N, D)
+    _, N, D = q.shape
+    return (skv_or_tkv, N, D)
+
+
+def check_shapes(q, k, v, out, softmax_lse, layout, *, atten_mask=None, mask_bcast=None) -> None:
+    """Raises ValueError unless k, v, out, softmax_lse (and atten_mask, when given) have the
+    shapes the C ABI derives from q and k: every extent the kernels use comes from q's and k's
+    shapes, so a shorter v, out, lse or mask would be read or written past its end."""
+    lay = _layout_code(layout)
+    want_dim = 3 if lay == 2 else 4
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t is not None and t.dim() != want_dim:
+            raise ValueError(f"{name} must be {want_dim}-D in layout {layout}, got {tuple(t.shape)}")
+    skv = k.shape[0] if lay == 2 else (k.shape[2] if lay == 0 else k.shape[1])
+    kv_want = _kv_shape_of(q, layout, skv)
+    if tuple(k.shape) != kv_want:
+        raise ValueError(f"k must have shape {kv_want} for q {tuple(q.shape)} ({layout}), got {tuple(k.shape)}")
+    if v is not None and tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v must have k's shape {tuple(k.shape)}, got {tuple(v.shape)}")
+    if out is not None and tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    if softmax_lse is not None and tuple(softmax_lse.shape) != lse_shape(q, layout):
+        raise ValueError(f"softmax_lse must have shape {lse_shape(q, layout)}, got {tuple(softmax_lse.shape)}")
+    if atten_mask is not None:
+        if lay == 2:
+            raise ValueError("atten_mask needs the BNSD or BSND layout")
+        B = q.shape[0]
+        N = q.shape[1] if lay == 0 else q.shape[2]
+        Sq = q.shape[2] if lay == 0 else q.shape[1]
+        bc = list(mask_bcast) if mask_bcast is not None else [0, 0]
+        m_want = (1 if bc[0] else B, 1 if bc[1] else N, Sq, skv)
+        if tuple(atten_mask.shape) != m_want:
+            raise ValueError(f"atten_mask must have shape {m_want} (mask_bcast {bc}), got {tuple(atten_mask.shape)}")
+
+
 def fa_fwd_workspace_size(dims: FaDims, layout, sparse_mode: int, actual_seq_qlen=None,
                           actual_seq_kvlen=None) -> int:
     lib = load_library()
@@ -183,6 +227,7 @@ def fa_fwd(q, k, v, out, softmax_lse, *, layout="BNSD", sparse_mode: int = 0, pr
     """Calls fa_fwd on device tensors. Raises FaError on a non-zero status.
 
     alibi_mode: "right", "sqrt" or "left" (or the FA_ALIBI_* code)."""
+    check_shapes(q, k, v, out, softmax_lse, layout, atten_mask=atten_mask, mask_bcast=mask_bcast)
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         _check_device_tensor(name, t, q.dtype)
@@ -308,6 +353,22 @@ def fa_fwd_paged(q, key_cache, value_cache, block_table, out, softmax_lse, *, la
                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Calls fa_fwd_paged: K / V from paged caches through an int32 block table
     [B, max_blocks_per_seq]. kv_seqlen is Skv for BNSD / BSND (TND uses actual_seq_kvlen)."""
+    if q.dim() != (3 if _layout_code(layout) == 2 else 4):
+        raise ValueError(f"q has the wrong rank for layout {layout}: {tuple(q.shape)}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    if tuple(softmax_lse.shape) != lse_shape(q, layout):
+        raise ValueError(f"softmax_lse must have shape {lse_shape(q, layout)}, got {tuple(softmax_lse.shape)}")
+    if atten_mask is not None:
+        lay = _layout_code(layout)
+        if lay == 2:
+            raise ValueError("atten_mask needs the BNSD or BSND layout")
+        bc = list(mask_bcast) if mask_bcast is not None else [0, 0]
+        Nq = q.shape[1] if lay == 0 else q.shape[2]
+        Sq = q.shape[2] if lay == 0 else q.shape[1]
+        m_want = (1 if bc[0] else q.shape[0], 1 if bc[1] else Nq, Sq, int(kv_seqlen))
+        if tuple(atten_mask.shape) != m_want:
+            raise ValueError(f"atten_mask must have shape {m_want} (mask_bcast {bc}), got {tuple(atten_mask.shape)}")
     lib = load_library()
     for name, t in (("q", q), ("key_cache", key_cache), ("value_cache", value_cache), ("out", out)):
         _check_device_tensor(name, t, q.dtype)
@@ -373,6 +434,7 @@ def fa_bwd(q, k, v, out, softmax_lse, dout, dq, dk, dv, *, layout="BNSD", sparse
            workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Calls fa_bwd: dq, dk, dv (written in full) from the forward's inputs, its out and
     softmax_lse, and dout. Raises FaError on a non-zero status."""
+    check_shapes(q, k, v, out, softmax_lse, layout, atten_mask=atten_mask, mask_bcast=mask_bcast)
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _check_device_tensor(name, t, q.dtype)

@@ -1414,9 +1414,21 @@ __global__ __launch_bounds__(GN_BM) void fa_fwd_generic(const fa_kargs a, int de
 #pragma unroll
     for (int d = 0; d < DMAX; ++d) o[d] = 0.f;
     const int row_lo = fa_row_lo(g, row), row_hi = fa_row_hi(g, row);
-    const float slope2 = alibi ? a.slopes[h] * kLog2e : 0.f;
+    const float slope = alibi ? a.slopes[h] : 0.f;
+    const float slope2 = slope * kLog2e;
     const int off = g.skv - g.sq;
     const int aoff = a.alibi_left ? 0 : off;   // diagonal of the linear alibi bias
+    // Scores are formed relative to the bias at a reference key jr of the row: its last
+    // visible key when the slope is >= 0 (where a linear bias is largest), else its first. The
+    // bias at jr is the same for every key of the row, so it cancels out of O; it goes into the
+    // LSE at the end, in double. The part of each score that fp32 rounds is then only its
+    // distance from the reference, which is small where the row's largest terms are: a bias of
+    // slope x (a few thousand keys) no longer costs the LSE its last digits.
+    const int jr = slope >= 0.f ? row_hi : row_lo;
+    const int dr = row + off - jr;   // square-root bias: distance of jr from the diagonal
+    double lse_shift = 0.0;
+    if (alibi == 1) lse_shift = double(slope) * double(jr - row - aoff);
+    if (alibi == 2) lse_shift = -double(slope) * copysign(sqrt(fabs(double(dr))), double(dr));
     const uint8_t* mrow = dense ? a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs
                                 : nullptr;
     float m = -INFINITY, l = 0.f;
@@ -1459,10 +1471,23 @@ __global__ __launch_bounds__(GN_BM) void fa_fwd_generic(const fa_kargs a, int de
             const bool vis = dense ? (row_ok && j < g.skv && mrow[j] == 0) : (j >= row_lo && j <= row_hi);
             float sv = dot * a.scale_log2;
             if (alibi == 1) {
-                sv += slope2 * float(j - row - aoff);
+                sv = fmaf(slope2, float(j - jr), sv);   // bias(j) - bias(jr)
             } else if (alibi == 2) {
-                const float dd = float(row + off - j);   // square-root bias
-                sv -= slope2 * copysignf(__builtin_amdgcn_sqrtf(fabsf(dd)), dd);
+                // -slope (f(d) - f(dr)) with f(x) = sign(x) sqrt|x|, d = i + (Skv - Sq) - j. On one
+                // side of the diagonal the difference of square roots is (|d| - |dr|) / (sqrt|d| +
+                // sqrt|dr|), which keeps its relative accuracy when d is close to dr; across it the
+                // two magnitudes add.
+                const int d = row + off - j;
+                const float qd = sqrtf(fabsf(float(d))), qr = sqrtf(fabsf(float(dr)));
+                float diff;
+                if ((d >= 0) == (dr >= 0)) {
+                    const float den = qd + qr;
+                    diff = den > 0.f ? float(abs(d) - abs(dr)) / den : 0.f;
+                    diff = d >= 0 ? diff : -diff;
+                } else {
+                    diff = d >= 0 ? qd + qr : -(qd + qr);
+                }
+                sv = fmaf(-slope2, diff, sv);
             }
             sv = vis ? sv : -INFINITY;
             const float m_new = fmaxf(m, sv);
@@ -1477,7 +1502,9 @@ __global__ __launch_bounds__(GN_BM) void fa_fwd_generic(const fa_kargs a, int de
     }
     if (row_ok) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+        // LSE = bias(jr) + ln 2 (m + log2 l), assembled in double and rounded once.
+        a.lse[b * a.lse_bs + h * a.lse_hs + g.q_start + row] =
+            l > 0.f ? float(lse_shift + (double(m) + log2(double(l))) * 0.6931471805599453) : -INFINITY;
         T* op = static_cast<T*>(a.o) + b * a.q_bs + h * a.q_hs + (int64_t(g.q_start) + row) * a.q_rs;
 #pragma unroll
         for (int d = 0; d < DMAX; ++d)

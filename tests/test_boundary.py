@@ -487,3 +487,65 @@ def test_bwd_validation_and_workspace(lib):
     d0 = bnsd(B=0)
     assert lib.fa_bwd(None, None, None, None, None, None, None, None, None, ctypes.byref(d0), 0, 3, 0, 0, None, None,
                       None, None, 0, None, None, 0.125, None, 0, None) == OK
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The binding checks every shape the C ABI derives from q and k (it has no other way to
+    know a buffer's length) before it looks at devices or calls the library: CPU tensors are
+    enough to reach each check."""
+    import torch
+
+    def t(*shape, dtype=torch.bfloat16):
+        return torch.zeros(shape, dtype=dtype)
+
+    B, N, Sq, Skv, D = 2, 3, 5, 7, 16
+    q, k, v, o = t(B, N, Sq, D), t(B, N, Skv, D), t(B, N, Skv, D), t(B, N, Sq, D)
+    lse = t(B, N, Sq, dtype=torch.float32)
+    fb.check_shapes(q, k, v, o, lse, "BNSD")                       # consistent: no error
+    bad = [
+        dict(v=t(B, N, Skv - 1, D)),                               # short v
+        dict(k=t(B, N + 1, Skv, D), v=t(B, N + 1, Skv, D)),        # k heads differ from q
+        dict(k=t(B, N, Skv, D + 8), v=t(B, N, Skv, D + 8)),        # k head size differs
+        dict(out=t(B, N, Sq - 1, D)),                              # short out
+        dict(softmax_lse=t(B, N, Sq - 1, dtype=torch.float32)),    # short lse
+        dict(softmax_lse=t(B, Sq, N, dtype=torch.float32)),        # lse not [B, N, Sq]
+    ]
+    for change in bad:
+        args = dict(q=q, k=k, v=v, out=o, softmax_lse=lse)
+        args.update(change)
+        with pytest.raises(ValueError):
+            fb.check_shapes(args["q"], args["k"], args["v"], args["out"], args["softmax_lse"], "BNSD")
+        with pytest.raises(ValueError):
+            fb.fa_fwd(args["q"], args["k"], args["v"], args["out"], args["softmax_lse"], layout="BNSD",
+                      sparse_mode=3, scale=0.25)
+    # dense mask: [B | 1, N | 1, Sq, Skv] as mask_bcast says
+    m = torch.zeros(B, N, Sq, Skv, dtype=torch.uint8)
+    fb.check_shapes(q, k, v, o, lse, "BNSD", atten_mask=m, mask_bcast=[0, 0])
+    fb.check_shapes(q, k, v, o, lse, "BNSD", atten_mask=m[:1], mask_bcast=[1, 0])
+    fb.check_shapes(q, k, v, o, lse, "BNSD", atten_mask=m[:, :1], mask_bcast=[0, 1])
+    for mask, bc in ((m[:, :, :, :-1], [0, 0]), (m[:1], [0, 0]), (m, [1, 0]), (m[:, :1], [1, 1])):
+        with pytest.raises(ValueError):
+            fb.check_shapes(q, k, v, o, lse, "BNSD", atten_mask=mask, mask_bcast=bc)
+        with pytest.raises(ValueError):
+            fb.fa_fwd(q, k, v, o, lse, layout="BNSD", sparse_mode=1, scale=0.25, atten_mask=mask,
+                      mask_bcast=bc)
+    # BSND and TND
+    qs, ks = t(B, Sq, N, D), t(B, Skv, N, D)
+    fb.check_shapes(qs, ks, ks.clone(), qs.clone(), lse, "BSND")
+    with pytest.raises(ValueError):
+        fb.check_shapes(qs, ks, t(B, Skv, N - 1, D), qs.clone(), lse, "BSND")
+    qt, kt = t(11, N, D), t(13, N, D)
+    lt = t(N, 11, dtype=torch.float32)
+    fb.check_shapes(qt, kt, kt.clone(), qt.clone(), lt, "TND")
+    for args in ((qt, kt, t(12, N, D), qt, lt), (qt, kt, kt, t(10, N, D), lt), (qt, kt, kt, qt, t(11, N, dtype=torch.float32))):
+        with pytest.raises(ValueError):
+            fb.check_shapes(*args, "TND")
+    with pytest.raises(ValueError):
+        fb.check_shapes(qt, kt, kt, qt, lt, "TND", atten_mask=torch.zeros(1, 1, 11, 13, dtype=torch.uint8))
+    # the backward takes the same checks
+    with pytest.raises(ValueError):
+        fb.fa_bwd(q, k, t(B, N, Skv - 2, D), o, lse, o.clone(), q.clone(), k.clone(), k.clone(),
+                  layout="BNSD", sparse_mode=3, scale=0.25)
+    with pytest.raises(ValueError):
+        fb.fa_bwd(q, k, v, o, t(B, N, 1, dtype=torch.float32), o.clone(), q.clone(), k.clone(), k.clone(),
+                  layout="BNSD", sparse_mode=3, scale=0.25)

@@ -177,3 +177,52 @@ def test_bwd_full_size_heads(gpu_device):
                                         sparse_mode=3, scale=w.softmax_scale)
         for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
             check_grad(got[sl].cpu(), r, torch.bfloat16, f"causal_8192 b={b} h={h} {name}")
+
+
+def test_bwd_delta_values(gpu_device):
+    """Delta = rowsum(dO * O), read back from a caller-owned workspace and compared with an fp64
+    sum of the same two rounded tensors, for the 16-byte vector kernel (BNSD, BSND, TND) and the
+    scalar one (D not a multiple of 8; an O that is not 16-byte aligned). Delta lives where the
+    library puts it: laid out like softmax_lse, at offset 0, or after the per-batch geometry
+    table (B entries of 32 bytes, rounded up to 256) in TND and prefix modes.
+
+    Bound: the products of two 16-bit floats are exact in fp32; a sum of D of them in fp32 is
+    within D 2^-24 of the sum of their magnitudes, so |d| <= 2^-17 sum|dO O| with D <= 128."""
+    cases = [("BNSD", "bf16", 128, False), ("BSND", "f16", 64, False), ("TND", "bf16", 128, False),
+             ("BNSD", "bf16", 36, False), ("BNSD", "bf16", 128, True)]
+    for layout, dtype, D, misalign in cases:
+        qlens = kvlens = None
+        kw = {}
+        B, N, sq, skv = 2, 3, 150, 170
+        if layout == "TND":
+            qlens, kvlens = [100, 0, 37], [120, 9, 37]
+            B = len(qlens)
+            kw = dict(actual_seq_qlen=synth.cumulative_ends(qlens), actual_seq_kvlen=synth.cumulative_ends(kvlens))
+        q, k, v = make_inputs(layout, dtype, B, N, sq, skv, D, seed=600 + D, qlens=qlens, kvlens=kvlens)
+        do = synth.randn(tuple(q.shape), DT[dtype], 601 + D)
+        qd, kd, vd, dod = (x.to(gpu_device) for x in (q, k, v, do))
+        print(f"[case] delta {layout} {dtype} D={D} misaligned O={misalign}", flush=True)
+        out, lse = fb.flash_attention(qd, kd, vd, layout=layout, sparse_mode=3, scale=0.1, **kw)
+        if misalign:
+            buf = torch.empty(out.numel() + 1, dtype=out.dtype, device=gpu_device)
+            moved = buf[1:].view(out.shape)
+            moved.copy_(out)
+            out = moved
+            assert out.data_ptr() % 16 != 0
+        dims = fb.dims_of(qd, kd, layout, kw.get("actual_seq_qlen"))
+        ws_bytes = fb.fa_bwd_workspace_size(dims, layout, 3, kw.get("actual_seq_qlen"), kw.get("actual_seq_kvlen"))
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=gpu_device)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        fb.fa_bwd(qd, kd, vd, out, lse, dod, dq, dk, dv, layout=layout, sparse_mode=3, scale=0.1, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        off = ((B * 32 + 255) // 256) * 256 if layout == "TND" else 0
+        n = lse.numel()
+        delta = ws[off:off + 4 * n].cpu().view(torch.float32).reshape(lse.shape).double().numpy()
+        prod = to64(dod) * to64(out)
+        ref, mag = prod.sum(-1), np.abs(prod).sum(-1)
+        if layout == "BSND":
+            ref, mag = ref.transpose(0, 2, 1), mag.transpose(0, 2, 1)
+        if layout == "TND":
+            ref, mag = ref.T, mag.T
+        err = np.abs(delta - ref)
+        assert (err <= 2.0 ** -17 * mag + 1e-30).all(), f"{layout} {dtype} D={D}: max |d| {err.max()}"
