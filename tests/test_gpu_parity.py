@@ -10,10 +10,11 @@ The oracle computes on the exact values the GPU sees: the library takes the soft
 the alibi slopes as fp32, so both reach the oracle rounded to fp32 (a slope of 0.6 is
 0.60000002384 on the device; over 200 keys that alone moves a bias by 5e-6).
 
-The fp32 LSE bound is absolute. An fp32 number holds an LSE of magnitude X to within
-X 2^-24 (half an ulp), 7.6e-6 at X = 128; the kernels add the large per-row part of an alibi
-bias in double, so what they add to that rounding is small next to it. Every fp32 case here
-keeps |LSE| below 128.
+The fp32 LSE bound is absolute. An fp32 number holds an LSE of magnitude X < 256 to within
+half an ulp, at most 2^-17 = 7.6e-6; the kernels add the large per-row part of an alibi bias
+in double, so what their fp32 arithmetic adds to that rounding is small next to it (an fp32
+emulation of the left-aligned band case at |LSE| = 129 gives 7.4e-6 in all). Past 256 half an
+ulp alone exceeds 1e-5, so every fp32 case here keeps |LSE| below 256.
 """
 
 import math
@@ -59,7 +60,7 @@ def check(o, lse, ref_o, ref_lse, dtype, what=""):
         err = np.abs(o - ref_o)
         assert err.max(initial=0) <= 1e-5, f"{what}: max |dO| {err.max()}"
         lse_err = np.abs(lse[live] - ref_lse[live])
-        assert np.abs(ref_lse[live]).max(initial=0) < 128, f"{what}: |LSE| past the range of the bound"
+        assert np.abs(ref_lse[live]).max(initial=0) < 256, f"{what}: |LSE| past the range of the bound"
         assert lse_err.max(initial=0) <= 1e-5, f"{what}: max |dLSE| {lse_err.max(initial=0)}"
     else:
         bound = 2e-2 + 1e-2 * np.abs(ref_o)
