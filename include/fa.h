@@ -128,6 +128,30 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  const uint8_t* atten_mask, const int64_t* mask_bcast,
                  float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* fa_fwd for callers that cannot allocate device memory: code under HIP graph capture,
+ * serving loops and harnesses that forbid hipMalloc. The arguments, validation, status codes
+ * and results are fa_fwd's (bitwise: the same kernels run), without the workspace pair: the
+ * workspace fa_fwd_workspace_size would ask for lives in a device array of this library, one
+ * copy per GPU, FA_NOALLOC_SCRATCH_BYTES long and held until the process ends.
+ * - A problem that needs more than FA_NOALLOC_SCRATCH_BYTES of workspace returns
+ *   FA_ERR_WORKSPACE before any device work (use fa_fwd with a workspace of its own).
+ * - stream must belong to the current device (else FA_ERR_PARAM_INVALID), whose copy of the
+ *   array is used.
+ * - The call allocates nothing (no hipMalloc, no hipFree). Every call on one GPU shares that
+ *   GPU's array, and the array keeps the last call's contents: calls that overlap on one GPU
+ *   (on different streams, or from several threads without ordering) race and may corrupt
+ *   each other's results. Nothing in it needs to start at zero: each call writes what it
+ *   reads. */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+fa_status fa_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* softmax_lse,
+                         const fa_dims* dims, int32_t layout, int32_t sparse_mode,
+                         int64_t pre_tokens, int64_t next_tokens,
+                         const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                         const int64_t* prefix, const float* alibi_slopes, int32_t alibi_mode,
+                         const uint8_t* atten_mask, const int64_t* mask_bcast,
+                         float scale, void* stream);
+
 /* Backward pass: gradients of a loss with respect to q, k and v, given dout = dLoss/dO. No
  * page gives a backward pass; this is the derivative of the forward defined above. With P
  * recomputed from q, k, the bias and the mask, and the forward's softmax_lse:

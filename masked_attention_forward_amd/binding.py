@@ -98,6 +98,9 @@ def load_library():
     lib.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
                                  vp, i32, vp, pi64, ppaged, ctypes.c_float, vp, sz, vp]
     lib.fa_fwd_paged.restype = i32
+    lib.fa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
+                                   vp, i32, vp, pi64, ctypes.c_float, vp]
+    lib.fa_fwd_noalloc.restype = i32
     lib.fa_bwd_workspace_size.argtypes = [pdims, i32, i32, pi64, pi64, ctypes.POINTER(sz)]
     lib.fa_bwd_workspace_size.restype = i32
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
@@ -246,6 +249,36 @@ def fa_fwd(q, k, v, out, softmax_lse, *, layout="BNSD", sparse_mode: int = 0, pr
                     stream if stream is not None else _stream(q.device))
     if st != 0:
         raise FaError(st, "fa_fwd")
+
+
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def fa_fwd_noalloc(q, k, v, out, softmax_lse, *, layout="BNSD", sparse_mode: int = 0, pre_tokens: int = 0,
+                   next_tokens: int = 0, actual_seq_qlen=None, actual_seq_kvlen=None, prefix=None,
+                   alibi_slopes: Optional[torch.Tensor] = None, alibi_mode="right",
+                   atten_mask: Optional[torch.Tensor] = None, mask_bcast=None, scale: float, stream=None) -> None:
+    """Calls fa_fwd_noalloc: fa_fwd with its workspace in the library's own device array (no
+    allocation anywhere). Raises FaError on a non-zero status (FA_ERR_WORKSPACE when the
+    problem needs more than FA_NOALLOC_SCRATCH_BYTES of workspace)."""
+    check_shapes(q, k, v, out, softmax_lse, layout, atten_mask=atten_mask, mask_bcast=mask_bcast)
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_device_tensor(name, t, q.dtype)
+    _check_device_tensor("softmax_lse", softmax_lse, torch.float32)
+    _check_device_tensor("alibi_slopes", alibi_slopes, torch.float32)
+    if atten_mask is not None:
+        _check_device_tensor("atten_mask", atten_mask)
+        if atten_mask.dtype not in (torch.uint8, torch.bool):
+            raise TypeError("atten_mask must be uint8 or bool")
+    dims = dims_of(q, k, layout, actual_seq_qlen)
+    st = lib.fa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(softmax_lse), ctypes.byref(dims),
+                            _layout_code(layout), int(sparse_mode), int(pre_tokens), int(next_tokens),
+                            _i64(actual_seq_qlen), _i64(actual_seq_kvlen), _i64(prefix), _ptr(alibi_slopes),
+                            _alibi_code(alibi_mode), _ptr(atten_mask), _i64(mask_bcast), float(scale),
+                            stream if stream is not None else _stream(q.device))
+    if st != 0:
+        raise FaError(st, "fa_fwd_noalloc")
 
 
 ALIBI_MODES = {"right": 0, "sqrt": 1, "left": 2}

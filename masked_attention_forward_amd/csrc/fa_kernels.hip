@@ -41,6 +41,7 @@
 #include <type_traits>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "fa_device.h"
@@ -1802,6 +1803,80 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
     c.scale = scale;
     return run_fwd(c, q, k, v, out, softmax_lse, alibi_slopes, atten_mask, nullptr, workspace, workspace_bytes,
                    stream);
+}
+
+// ------------------------------------------------------------------------------------------
+// fa_fwd_noalloc: fa_fwd with the workspace in a fixed device array of this library.
+// ------------------------------------------------------------------------------------------
+
+namespace {
+
+// The workspace of fa_fwd_noalloc: one copy per GPU, held until the process ends. In host code
+// `scratch` names a host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only that address is
+// ever passed to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev`, which must be the current device.
+fa_status scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                    float* softmax_lse, const fa_dims* dims, int32_t layout,
+                                    int32_t sparse_mode, int64_t pre_tokens, int64_t next_tokens,
+                                    const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
+                                    const int64_t* prefix, const float* alibi_slopes, int32_t alibi_mode,
+                                    const uint8_t* atten_mask, const int64_t* mask_bcast, float scale,
+                                    void* stream) {
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = sparse_mode;
+    c.pre_tokens = pre_tokens;
+    c.next_tokens = next_tokens;
+    c.actual_seq_qlen = actual_seq_qlen;
+    c.actual_seq_kvlen = actual_seq_kvlen;
+    c.prefix = prefix;
+    c.has_alibi = alibi_slopes != nullptr;
+    c.alibi_mode = alibi_mode;
+    c.has_mask = atten_mask != nullptr;
+    c.mask_bcast = mask_bcast;
+    c.scale = scale;
+    // Validate and size first: a problem whose workspace would not fit is refused before any
+    // HIP call.
+    fa_plan p;
+    const fa_status st = fa_make_plan(c, false, &p);
+    if (st != FA_OK) return st;
+    if (p.ws_bytes > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (p.ws_bytes > 0) {
+        // The stream's device must be the current one: that is the copy of `scratch` whose
+        // address hipGetSymbolAddress returns.
+        int cur = -1;
+        hipDevice_t sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_HIP;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return FA_ERR_HIP;
+        if (sdev != cur) return FA_ERR_PARAM_INVALID;
+        const fa_status sa = scratch_address(cur, &ws);
+        if (sa != FA_OK) return sa;
+    }
+    return run_fwd(c, q, k, v, out, softmax_lse, alibi_slopes, atten_mask, nullptr, ws,
+                   ws ? size_t(FA_NOALLOC_SCRATCH_BYTES) : 0, stream);
 }
 
 extern "C" fa_status fa_fwd_paged(const void* q, const void* key_cache, const void* value_cache, void* out,

@@ -549,3 +549,24 @@ def test_binding_rejects_mismatched_shapes():
     with pytest.raises(ValueError):
         fb.fa_bwd(q, k, v, o, t(B, N, 1, dtype=torch.float32), o.clone(), q.clone(), k.clone(), k.clone(),
                   layout="BNSD", sparse_mode=3, scale=0.25)
+
+
+def test_noalloc_validates_and_refuses_oversize_before_device_work(lib):
+    """fa_fwd_noalloc validates like fa_fwd and refuses a problem whose workspace exceeds
+    FA_NOALLOC_SCRATCH_BYTES with FA_ERR_WORKSPACE, all before any HIP call (this host has
+    no GPU, so reaching one would fail differently)."""
+    buf = (ctypes.c_char * 4096)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    n = 600_000
+    ends = list(range(1, n + 1))
+    d = tnd([1] * n, [1] * n)
+    assert fb.fa_fwd_workspace_size(d, "TND", 3, ends, ends) > fb.FA_NOALLOC_SCRATCH_BYTES
+    st = lib.fa_fwd_noalloc(p, p, p, p, p, ctypes.byref(d), 2, 3, 0, 0, fb._i64(ends), fb._i64(ends), None,
+                            None, 0, None, None, 0.125, None)
+    assert st == WORKSPACE
+    st = lib.fa_fwd_noalloc(p, p, p, p, p, ctypes.byref(bnsd()), 0, 4, 3, -9, None, None, None, None, 0, None,
+                            None, 0.125, None)
+    assert st == INVALID
+    st = lib.fa_fwd_noalloc(None, p, p, p, p, ctypes.byref(bnsd()), 0, 3, 0, 0, None, None, None, None, 0, None,
+                            None, 0.125, None)
+    assert st == NULLPTR
