@@ -115,9 +115,11 @@ def visible_pairs(w, dev) -> int:
     q = torch.empty(qk[0], dtype=synth.DTYPES[w.dtype], device="meta")
     k = torch.empty(qk[1], dtype=synth.DTYPES[w.dtype], device="meta")
     dims = fb.dims_of(q, k, w.layout, w.actual_seq_qlen)
+    mask, bcast = w.mask()
     counts, _ = fb.fa_mask_probe(dims, w.layout, w.sparse_mode, device=dev, pre_tokens=w.pre_tokens,
                                  next_tokens=w.next_tokens, actual_seq_qlen=w.actual_seq_qlen,
-                                 actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix, tiles=False)
+                                 actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix, tiles=False,
+                                 atten_mask=None if mask is None else mask.to(dev), mask_bcast=bcast)
     total = int(counts.sum().item())
     if w.sparse_mode == 3 and w.layout != "TND" and w.Sq <= w.Skv:
         per_head = w.Sq * (w.Skv - w.Sq) + w.Sq * (w.Sq + 1) // 2
@@ -136,6 +138,8 @@ def cpu_baseline(w, heads: int, decode: bool = False):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     q, k, v = w.tensors()
+    mask, _ = w.mask()
+    mask = None if mask is None else mask.numpy()   # [1, 1, Sq, Skv]: shared by every slice
     assert w.layout == "BNSD"
     sel = [(b, h) for b in range(w.B) for h in range(w.N)][:heads]
     flops = 0
@@ -149,11 +153,15 @@ def cpu_baseline(w, heads: int, decode: bool = False):
         t0 = time.perf_counter()
         _, lse = oracle.attention(qs, ks, vs, layout="BNSD", sparse_mode=w.sparse_mode,
                                   scale=w.softmax_scale, pre_tokens=w.pre_tokens,
-                                  next_tokens=w.next_tokens, prefix=prefix, alibi_slopes=slopes)
+                                  next_tokens=w.next_tokens, prefix=prefix, alibi_slopes=slopes,
+                                  atten_mask=mask)
         t_total += time.perf_counter() - t0
-        vis = oracle.visible_matrix(w.sparse_mode, w.Sq, w.Skv, pre_tokens=w.pre_tokens,
-                                    next_tokens=w.next_tokens,
-                                    prefix_len=prefix[0] if prefix else 0)
+        if mask is not None:
+            vis = mask[0, 0] == 0
+        else:
+            vis = oracle.visible_matrix(w.sparse_mode, w.Sq, w.Skv, pre_tokens=w.pre_tokens,
+                                        next_tokens=w.next_tokens,
+                                        prefix_len=prefix[0] if prefix else 0)
         flops += 4 * w.D * int(vis.sum())
     if decode:
         elem = q.element_size()
@@ -357,6 +365,8 @@ def main():
     w = synth.workloads()[args.workload]
     q, k, v = (x.to(dev) for x in w.tensors())
     slopes = torch.tensor(w.slopes(), dtype=torch.float32, device=dev) if w.alibi else None
+    mask, mask_bcast = w.mask()
+    mask = None if mask is None else mask.to(dev)
     out = torch.empty_like(q)
     lse = torch.empty(fb.lse_shape(q, w.layout), dtype=torch.float32, device=dev)
     dims = fb.dims_of(q, k, w.layout, w.actual_seq_qlen)
@@ -366,13 +376,15 @@ def main():
         pk = fb.paged_kv(paged[2], paged[0], cache_layout=args.cache_layout)
         ws_bytes = fb.fa_fwd_paged_workspace_size(dims, w.layout, w.sparse_mode, pk, w.actual_seq_qlen,
                                                   w.actual_seq_kvlen)
+    elif w.sparse_mode == 1:
+        ws_bytes = fb.fa_fwd_mask_workspace_size(dims, w.layout, mask_bcast)
     else:
         ws_bytes = fb.fa_fwd_workspace_size(dims, w.layout, w.sparse_mode, w.actual_seq_qlen, w.actual_seq_kvlen)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     kw = dict(layout=w.layout, sparse_mode=w.sparse_mode, pre_tokens=w.pre_tokens, next_tokens=w.next_tokens,
               actual_seq_qlen=w.actual_seq_qlen, actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix,
               alibi_slopes=slopes, alibi_mode=args.alibi_mode, scale=w.softmax_scale,
-              workspace=ws if ws_bytes else None)
+              atten_mask=mask, mask_bcast=mask_bcast, workspace=ws if ws_bytes else None)
     if paged is not None:
         kc, vc, bt = paged
         pkw = dict(kw, cache_layout=args.cache_layout, kv_seqlen=w.Skv)

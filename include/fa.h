@@ -103,10 +103,24 @@ typedef struct fa_dims {
  * Rows with no visible column produce O = 0 and LSE = -inf. */
 
 /* Phase 1: validate the sizes and return the workspace size fa_fwd needs (in bytes; 0 means
- * no workspace). Host only; never touches the GPU. */
+ * no workspace). Host only; never touches the GPU.
+ * What the workspace holds: the per-batch geometry and work list in TND and prefix modes
+ * (modes 5, 6), the split-KV partial results of short-query problems, and in mode 1 (on the
+ * MFMA kernels) the tile map a pre-pass builds from atten_mask: per (q tile, kv tile) its
+ * class, per q tile the list of kv tiles with a visible entry (the kernel loads no other), and
+ * the mask bits packed in the order the kernel reads them, about an eighth of the mask's own
+ * size. For mode 1 this query assumes an unbroadcast mask, the largest case; see
+ * fa_fwd_mask_workspace_size. */
 fa_status fa_fwd_workspace_size(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
                                 const int64_t* actual_seq_qlen, const int64_t* actual_seq_kvlen,
                                 size_t* bytes);
+
+/* The workspace size of a mode-1 (atten_mask) call whose mask broadcast is known: mask_bcast
+ * as for fa_fwd (NULL = unbroadcast). A mask shared over batches and heads ([1, 1, Sq, Skv])
+ * needs 1 / (B N) of what fa_fwd_workspace_size returns for mode 1. fa_fwd accepts any
+ * workspace at least this large. Host only. */
+fa_status fa_fwd_mask_workspace_size(const fa_dims* dims, int32_t layout, const int64_t* mask_bcast,
+                                     size_t* bytes);
 
 /* Phase 2: the forward pass.
  *   q, k, v, out:  device, dims->dtype, in `layout`.
@@ -189,7 +203,11 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out,
  *                       it), 1 = visited with per-element masking, 2 = visited without
  *                       masking (every in-range entry visible), 3 = outside the sequence.
  *                       Row r of the map is the q tile r of the batch-major enumeration
- *                       (batch 0's tiles first). Mode 1 is not tiled (NULL required).
+ *                       (batch 0's tiles first). In mode 1 the classes come from atten_mask
+ *                       and differ per head: the map is [B * N * n_qtiles_per_batch,
+ *                       n_kvtiles_max], rows ordered by batch, then head, then q tile; mode 1
+ *                       has a map only where fa_fwd runs the pre-pass (fp16 / bf16 with
+ *                       D = 64 or 128), else tile_class must be NULL (FA_ERR_UNSUPPORTED).
  * The workspace argument has fa_fwd's meaning and size. Asynchronous on `stream`. */
 fa_status fa_mask_probe(const fa_dims* dims, int32_t layout, int32_t sparse_mode,
                         int64_t pre_tokens, int64_t next_tokens,

@@ -98,6 +98,8 @@ def load_library():
     lib.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
                                  vp, i32, vp, pi64, ppaged, ctypes.c_float, vp, sz, vp]
     lib.fa_fwd_paged.restype = i32
+    lib.fa_fwd_mask_workspace_size.argtypes = [pdims, i32, pi64, ctypes.POINTER(sz)]
+    lib.fa_fwd_mask_workspace_size.restype = i32
     lib.fa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
                                    vp, i32, vp, pi64, ctypes.c_float, vp]
     lib.fa_fwd_noalloc.restype = i32
@@ -219,6 +221,18 @@ def fa_fwd_workspace_size(dims: FaDims, layout, sparse_mode: int, actual_seq_qle
                                    _i64(actual_seq_qlen), _i64(actual_seq_kvlen), ctypes.byref(out))
     if st != 0:
         raise FaError(st, "fa_fwd_workspace_size")
+    return int(out.value)
+
+
+def fa_fwd_mask_workspace_size(dims: FaDims, layout, mask_bcast=None) -> int:
+    """Workspace bytes of a mode-1 call with this mask broadcast (exact; fa_fwd_workspace_size
+    assumes an unbroadcast mask)."""
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    st = lib.fa_fwd_mask_workspace_size(ctypes.byref(dims), _layout_code(layout), _i64(mask_bcast),
+                                        ctypes.byref(out))
+    if st != 0:
+        raise FaError(st, "fa_fwd_mask_workspace_size")
     return int(out.value)
 
 
@@ -516,8 +530,11 @@ def flash_attention(q, k, v, *, layout="BNSD", sparse_mode: int = 0, scale: floa
     out = torch.empty_like(q)
     lse = torch.empty(lse_shape(q, layout), dtype=torch.float32, device=q.device)
     dims = dims_of(q, k, layout, kw.get("actual_seq_qlen"))
-    ws = fa_fwd_workspace_size(dims, layout, sparse_mode, kw.get("actual_seq_qlen"),
-                               kw.get("actual_seq_kvlen"))
+    if sparse_mode == 1:
+        ws = fa_fwd_mask_workspace_size(dims, layout, kw.get("mask_bcast"))
+    else:
+        ws = fa_fwd_workspace_size(dims, layout, sparse_mode, kw.get("actual_seq_qlen"),
+                                   kw.get("actual_seq_kvlen"))
     workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
     fa_fwd(q, k, v, out, lse, layout=layout, sparse_mode=sparse_mode, scale=scale,
            workspace=workspace, **kw)
@@ -563,10 +580,15 @@ def fa_mask_probe(dims: FaDims, layout, sparse_mode: int, *, device, pre_tokens=
     else:
         counts = torch.empty((dims.B, dims.N, dims.Sq), dtype=torch.int64, device=device)
     tile = None
-    if tiles and sparse_mode != 1:
+    if tiles:
         _, _, nq, nk = fa_tile_shape(dims, layout, actual_seq_qlen, actual_seq_kvlen)
+        if sparse_mode == 1:
+            nq *= dims.N    # mode 1: one map row per (batch, head, q tile)
         tile = torch.empty((nq, nk), dtype=torch.uint8, device=device)
-    ws = fa_fwd_workspace_size(dims, layout, sparse_mode, actual_seq_qlen, actual_seq_kvlen)
+    if sparse_mode == 1:
+        ws = fa_fwd_mask_workspace_size(dims, layout, mask_bcast)
+    else:
+        ws = fa_fwd_workspace_size(dims, layout, sparse_mode, actual_seq_qlen, actual_seq_kvlen)
     workspace = torch.empty(ws, dtype=torch.uint8, device=device) if ws else None
     st = lib.fa_mask_probe(ctypes.byref(dims), lay, int(sparse_mode), int(pre_tokens), int(next_tokens),
                            _i64(actual_seq_qlen), _i64(actual_seq_kvlen), _i64(prefix),

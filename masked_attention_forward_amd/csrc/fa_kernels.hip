@@ -78,6 +78,11 @@ struct fa_kargs {
     int32_t block_size;
     int32_t log2_block_size;      // ping-pong kernel: block_size = 2^log2_block_size >= 64
     int32_t num_pages;            // valid page ids are [0, num_pages)
+    // Dense mask (sparse mode 1) on the ping-pong kernel: the pre-pass's tables (workspace).
+    const uint32_t* tile_list;    // [slices, nqt, 1 + nkt]: count, then kt | full-wave bits << 24
+    const uint32_t* tile_bits;    // [slices, nqt, nkt, 512]: hidden-key bits, one dword per lane
+    int32_t dense_nqt, dense_nkt;
+    int32_t m_heads, m_bcast_b, m_bcast_h;
 };
 
 // Work item of this workgroup. Workgroups are dispatched round-robin over the 8 XCDs, each
@@ -508,6 +513,11 @@ fa_fwd_mfma(const fa_kargs a) {
 // Phase barriers order LDS only, so loads stay in flight across them.
 // ------------------------------------------------------------------------------------------
 
+// Dense-mask tile entries: the kv tile index in the low 24 bits; FA_DENSE_END (past the list)
+// names a tile past every key, whose loads read nothing.
+constexpr uint32_t FA_DENSE_KT = 0xFFFFFFu;
+constexpr uint32_t FA_DENSE_END = 0xFFFFFFFFu;
+
 constexpr int PP_BM = FA_PP_BM;   // 256 query rows per workgroup (8 waves x 32 rows)
 constexpr int PP_BN = FA_PP_BN;   // 64 keys per kv tile
 constexpr int PP_THREADS = 512;
@@ -572,8 +582,30 @@ fa_fwd_pp(const fa_kargs a) {
     const int i0 = qt * BM;
     const int i_last = min(i0 + BM, g.sq) - 1;
     const fa_kv_range kr = fa_tile_kv_range(g, i0, i_last, BN);
-    const int n_tiles = kr.end - kr.begin;
-    const int kv_lim = min(kr.end * BN, g.skv);
+    int n_tiles = kr.end - kr.begin;
+    int kv_lim = min(kr.end * BN, g.skv);
+    // Dense mask: the kv tiles come from the pre-pass's list for this q tile (a count, then per
+    // visited tile kt | full-wave bits << 24), and the per-element mask from its packed bits.
+    // Entries are read by scalar loads through the constant address space (the tables do not
+    // change during the kernel); past the count an entry is FA_DENSE_END, a tile past every key
+    // whose loads read nothing.
+    const __attribute__((address_space(4))) uint32_t* trec = nullptr;
+    const uint32_t* tbits = nullptr;
+    if constexpr (DENSE) {
+        n_tiles = 0;
+        kv_lim = g.skv;
+        if (a.tile_list) {
+            const int ms = (a.m_bcast_b ? 0 : b) * a.m_heads + (a.m_bcast_h ? 0 : h);
+            const int64_t r = int64_t(ms) * a.dense_nqt + qt;
+            trec = (const __attribute__((address_space(4))) uint32_t*)(a.tile_list + r * (a.dense_nkt + 1));
+            tbits = a.tile_bits + r * a.dense_nkt * 512 + wave * 64 + lane;
+            n_tiles = fa_uniform(int(trec[0]));
+        }
+    }
+    auto ent = [&](int t) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (DENSE) return t < n_tiles ? trec[1 + t] : FA_DENSE_END;
+        else return 0u;
+    };
 
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + h * a.q_hs +
                          (int64_t(g.q_start) + i0) * a.q_rs;
@@ -604,8 +636,6 @@ fa_fwd_pp(const fa_kargs a) {
     asm volatile("" : : "s"(sl2), "v"(slope2));
     const int off = g.skv - g.sq;
     const int aoff = a.alibi_left ? 0 : off;   // diagonal of the linear alibi bias
-    const uint8_t* mrow = nullptr;
-    if (DENSE) mrow = a.mask + b * a.m_bs + h * a.m_hs + int64_t(row_ok ? row : 0) * a.m_rs;
 
     // Paged K / V: a 64-key tile lies inside one page (pages hold 2^lbs >= 64 keys). Page ids
     // come straight from the block table with scalar loads, issued at the start of a softmax
@@ -635,6 +665,9 @@ fa_fwd_pp(const fa_kargs a) {
         }
     };
     int pg_v_next = 0, pg_k_next = 0;   // page ids of the next iteration's V and K loads
+    // Dense mask: entries of the next iteration's V and K loads, of the current and next tile,
+    // and the current tile's mask bits.
+    uint32_t e_v_next = 0u, e_k_next = 0u, e_cur = 0u, e_nxt = 0u, hid_cur = 0u;
 
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -705,20 +738,13 @@ fa_fwd_pp(const fa_kargs a) {
 
     // SM(t): mask, scale (+ alibi), online softmax update, P^T packed for the PV product. The
     // O^T rescale happens here too: no MFMA of this wave is using the accumulators.
-    auto softmax = [&](int t) __attribute__((always_inline)) {
-        const int j0 = (kr.begin + t) * BN;
-        const bool full = !DENSE && fa_tile_full(g, wrow0, wlast, j0, BN);
+    // es: the dense-mask entry of tile t; hidden: its packed mask bits for this lane.
+    auto softmax = [&](int t, uint32_t es, uint32_t hidden) __attribute__((always_inline)) {
+        const int j0 = DENSE ? int(es & FA_DENSE_KT) * BN : (kr.begin + t) * BN;
+        const bool full = DENSE ? ((es >> (24 + wave_u)) & 1u) != 0u : fa_tile_full(g, wrow0, wlast, j0, BN);
         if (!full) {
             if (DENSE) {
-                // One byte per key; keys past Skv (and invalid rows) read nothing.
-                uint32_t hidden = 0;
-#pragma unroll
-                for (int e = 0; e < 32; ++e) {
-                    const int r = e & 15;
-                    const int j = j0 + 32 * (e >> 4) + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    const bool in = row_ok && j < g.skv;
-                    hidden |= uint32_t(!in || mrow[in ? j : 0] != 0) << e;
-                }
+                // Bit e hides this lane's key 32 (e / 16) + 8 ((e / 4) % 4) + 4 hl + e % 4 of the tile.
 #pragma unroll
                 for (int e = 0; e < 32; ++e)
                     sacc[e >> 4][e & 15] = (hidden >> e) & 1u ? -INFINITY : sacc[e >> 4][e & 15];
@@ -864,15 +890,33 @@ fa_fwd_pp(const fa_kargs a) {
             pg_v_next = page_of(kr.begin + t + 4);
             pg_k_next = page_of(kr.begin + t + 5);
         }
-        softmax(t);
+        // Dense mask: entries of V(t + 3) and K(t + 4) were fetched one iteration ago (V(t + 4) is
+        // this iteration's K), tile t + 1's two. Fetch K(t + 5) and tile t + 2.
+        const uint32_t e_v = e_v_next, e_k = e_k_next, e_s = e_cur;
+        uint32_t e_far = 0u;
+        if constexpr (DENSE) {
+            e_v_next = e_k_next;
+            e_k_next = ent(t + 5);
+            e_far = ent(t + 2);
+        }
+        softmax(t, e_s, hid_cur);
+        // Tile t + 1's mask bits for the next softmax, when this wave masks it: the load has the
+        // matrix phase to land (its closing wait covers every load issued before the tile batch).
+        if constexpr (DENSE) {
+            if (e_nxt != FA_DENSE_END && !((e_nxt >> (24 + wave_u)) & 1u))
+                hid_cur = __builtin_nontemporal_load(tbits + int64_t(e_nxt & FA_DENSE_KT) * 512);
+            e_cur = e_nxt;
+            e_nxt = e_far;
+        }
         // The scalar loads land here, while no LDS read is in flight.
         if constexpr (PAGED) asm volatile("" : : "s"(pg_v_next), "s"(pg_k_next));
+        if constexpr (DENSE) asm volatile("" : : "s"(e_v_next), "s"(e_k_next), "s"(e_nxt));
         prefetch(v_cur);
         fa_lds_barrier_pending<2 * NPRE>();   // the prefetched V^T reads may still be in flight
         __builtin_amdgcn_s_setprio(1);
         matmul(k_cur, v_cur, [&]() __attribute__((always_inline)) {
-            dload(vp, kr.begin + t + 3, pg_v, v_fill);
-            dload(kp, kr.begin + t + 4, pg_k, k_fill);
+            dload(vp, DENSE ? int(e_v & FA_DENSE_KT) : kr.begin + t + 3, pg_v, v_fill);
+            dload(kp, DENSE ? int(e_k & FA_DENSE_KT) : kr.begin + t + 4, pg_k, k_fill);
         });
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(fa_vmcnt(BATCH));
@@ -886,13 +930,26 @@ fa_fwd_pp(const fa_kargs a) {
         const int pg2 = page_of(kr.begin + 2), pg3 = page_of(kr.begin + 3);
         pg_v_next = pg3;
         pg_k_next = page_of(kr.begin + 4);
-        dload(kp, kr.begin, pg0, lds_k3);
-        dload(vp, kr.begin, pg0, lds_v0);
-        dload(kp, kr.begin + 1, pg1, lds_k0);
-        dload(vp, kr.begin + 1, pg1, lds_v1);
-        dload(kp, kr.begin + 2, pg2, lds_k1);
-        dload(vp, kr.begin + 2, pg2, lds_v2);
-        dload(kp, kr.begin + 3, pg3, lds_k2);
+        int kt0 = kr.begin, kt1 = kr.begin + 1, kt2 = kr.begin + 2, kt3 = kr.begin + 3;
+        if constexpr (DENSE) {
+            const uint32_t e0 = ent(0), e1 = ent(1), e2 = ent(2), e3 = ent(3);
+            kt0 = int(e0 & FA_DENSE_KT);
+            kt1 = int(e1 & FA_DENSE_KT);
+            kt2 = int(e2 & FA_DENSE_KT);
+            kt3 = int(e3 & FA_DENSE_KT);
+            e_v_next = e3;
+            e_k_next = ent(4);
+            e_cur = e0;
+            e_nxt = e1;
+            if (!((e0 >> (24 + wave_u)) & 1u)) hid_cur = __builtin_nontemporal_load(tbits + int64_t(kt0) * 512);
+        }
+        dload(kp, kt0, pg0, lds_k3);
+        dload(vp, kt0, pg0, lds_v0);
+        dload(kp, kt1, pg1, lds_k0);
+        dload(vp, kt1, pg1, lds_v1);
+        dload(kp, kt2, pg2, lds_k1);
+        dload(vp, kt2, pg2, lds_v2);
+        dload(kp, kt3, pg3, lds_k2);
         __builtin_amdgcn_s_waitcnt(0);
         fa_lds_barrier();
         if (grp == 0) {
@@ -1554,6 +1611,141 @@ __global__ void fa_probe_tiles(const fa_kargs a, uint8_t* tile_class, int64_t n_
 }
 
 // ------------------------------------------------------------------------------------------
+// Dense mask (sparse mode 1) pre-pass for the ping-pong kernel. "sparseMode介绍", section
+// sparseMode=1, hands the kernel a complete attenMask (non-zero = masked). The pre-pass reads it
+// once and, per mask slice (batch or 1, head or 1), q tile of 256 rows and kv tile of 64 keys:
+//  * packs the tile's mask bits in the order the kernel's lanes consume them: lane l of wave w
+//    holds query row 32 w + l % 32 and, in bit e, key 32 (e / 16) + 8 ((e / 4) % 4) + 4 (l / 32)
+//    + e % 4 (1 = hidden: masked, past Skv, or a row past Sq), so a lane reads one dword;
+//  * classifies the tile: any visible entry, and per 32-row block whether every entry is
+//    visible (that wave then skips per-element masking);
+// then lists, per q tile, the kv tiles with a visible entry. The kernel loads no other tile.
+// ------------------------------------------------------------------------------------------
+
+struct fa_mask_args {
+    const uint8_t* mask;
+    int64_t m_bs, m_hs, m_rs;   // element strides of the mask (0 for a broadcast dimension)
+    int32_t sq, skv;
+    int32_t nqt, nkt;           // q tiles (256 rows) and kv tiles (64 keys) per slice
+    int32_t m_heads;            // heads of the mask (N, or 1 when broadcast)
+    uint16_t* cls;              // [slices, nqt, nkt]: bit 0 any visible, bits 8-15 full per block
+    uint32_t* lists;            // [slices, nqt, 1 + nkt]: count, then kt | full bits << 24
+    uint32_t* bits;             // [slices, nqt, nkt, 512]
+};
+
+constexpr int MC_TILES = 4;   // kv tiles per classify workgroup
+
+// Hidden bits (1 = masked) of four mask bytes: bit c for byte c.
+__device__ __forceinline__ uint32_t fa_nonzero_bytes(uint32_t x) {
+    const uint32_t t = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;   // bit 7 of each byte: byte != 0
+    return ((t >> 7) & 1u) | ((t >> 14) & 2u) | ((t >> 21) & 4u) | ((t >> 28) & 8u);
+}
+
+// One 256-thread workgroup per (MC_TILES kv tiles, q tile, slice); thread r takes row r of the
+// q tile. ALIGNED: rows start on 16-byte boundaries (Skv % 16 == 0 and an aligned base), so a
+// row's 64 bytes of a tile are four 16-byte loads; otherwise bytes are read one by one.
+template <bool ALIGNED>
+__global__ __launch_bounds__(256) void fa_mask_classify(const fa_mask_args m) {
+    __shared__ uint32_t red[MC_TILES][8];   // per tile and 32-row block: bit 0 any visible, bit 1 all
+    const int qt = blockIdx.y, ms = blockIdx.z;
+    const int kt0 = blockIdx.x * MC_TILES;
+    const int rho = threadIdx.x, lane = rho & 63, wv = rho >> 6;
+    const int row = qt * FA_PP_BM + rho;
+    const bool row_ok = row < m.sq;
+    const uint8_t* mrow = m.mask + int64_t(ms / m.m_heads) * m.m_bs + int64_t(ms % m.m_heads) * m.m_hs +
+                          int64_t(row_ok ? row : 0) * m.m_rs;
+    const int64_t tile0 = (int64_t(ms) * m.nqt + qt) * m.nkt;
+    for (int i = 0; i < MC_TILES; ++i) {
+        const int kt = kt0 + i;
+        if (kt >= m.nkt) break;
+        const int j0 = kt * FA_PP_BN;
+        // hid[hl], bit 4 (q / 2) + c: key 4 q + c of the tile (q = 0..15 its 4-byte words; word
+        // q belongs to lane half hl = q % 2).
+        uint32_t hid[2] = {0xFFFFFFFFu, 0xFFFFFFFFu};
+        if (row_ok) {
+            uint32_t w[16];
+            if constexpr (ALIGNED) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    u32x4 x = {0u, 0u, 0u, 0u};
+                    if (j0 + 16 * c < m.skv) x = *reinterpret_cast<const u32x4*>(mrow + j0 + 16 * c);
+                    w[4 * c + 0] = x[0]; w[4 * c + 1] = x[1]; w[4 * c + 2] = x[2]; w[4 * c + 3] = x[3];
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    uint32_t x = 0;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int j = j0 + 4 * q + c;
+                        x |= uint32_t(j < m.skv ? mrow[j] : 0) << (8 * c);
+                    }
+                    w[q] = x;
+                }
+            }
+            hid[0] = hid[1] = 0u;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int in = m.skv - (j0 + 4 * q);   // keys of this word inside the sequence
+                const uint32_t past = in >= 4 ? 0u : (0xFu << (in > 0 ? in : 0)) & 0xFu;
+                hid[q & 1] |= (fa_nonzero_bytes(w[q]) | past) << (4 * (q >> 1));
+            }
+        }
+        uint32_t* dst = m.bits + (tile0 + kt) * 512 + (rho >> 5) * 64 + (rho & 31);
+        dst[0] = hid[0];
+        dst[32] = hid[1];
+        const bool any = row_ok && (hid[0] != 0xFFFFFFFFu || hid[1] != 0xFFFFFFFFu);
+        const bool all = !row_ok || (hid[0] == 0u && hid[1] == 0u);
+        const uint64_t ba = __ballot(any), bf = __ballot(all);
+        if (lane == 0) {
+            red[i][2 * wv] = (uint32_t(ba) != 0u ? 1u : 0u) | (uint32_t(bf) == 0xFFFFFFFFu ? 2u : 0u);
+            red[i][2 * wv + 1] = (uint32_t(ba >> 32) != 0u ? 1u : 0u) | (uint32_t(bf >> 32) == 0xFFFFFFFFu ? 2u : 0u);
+        }
+    }
+    __syncthreads();
+    if (rho < MC_TILES && kt0 + rho < m.nkt) {
+        uint32_t any = 0u, full = 0u;
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            any |= red[rho][blk] & 1u;
+            full |= ((red[rho][blk] >> 1) & 1u) << blk;
+        }
+        m.cls[tile0 + kt0 + rho] = uint16_t(any | (full << 8));
+    }
+}
+
+// One wave per (q tile, slice): the kv tiles with a visible entry, in order.
+__global__ __launch_bounds__(64) void fa_mask_compact(const fa_mask_args m) {
+    const int qt = blockIdx.x, ms = blockIdx.y, lane = threadIdx.x;
+    const int64_t r = int64_t(ms) * m.nqt + qt;
+    const uint16_t* c = m.cls + r * m.nkt;
+    uint32_t* rec = m.lists + r * (m.nkt + 1);
+    int base = 0;
+    for (int k0 = 0; k0 < m.nkt; k0 += 64) {
+        const int kt = k0 + lane;
+        const uint32_t v = kt < m.nkt ? c[kt] : 0u;
+        const uint64_t bal = __ballot(v & 1u);
+        if (v & 1u) rec[1 + base + __popcll(bal & ((uint64_t(1) << lane) - 1))] = uint32_t(kt) | ((v >> 8) << 24);
+        base += __popcll(bal);
+    }
+    if (lane == 0) rec[0] = uint32_t(base);
+}
+
+// Mask probe of mode 1: tile classes of every (batch, head, q tile) from the pre-pass.
+__global__ void fa_probe_tiles_dense(const fa_mask_args m, uint8_t* tile_class, int64_t n_kv_max, int N,
+                                     int bcast_b, int bcast_h) {
+    const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int ms = (bcast_b ? 0 : b) * m.m_heads + (bcast_h ? 0 : h);
+    const uint16_t* c = m.cls + (int64_t(ms) * m.nqt + qt) * m.nkt;
+    uint8_t* out = tile_class + ((int64_t(b) * N + h) * m.nqt + qt) * n_kv_max;
+    for (int kt = threadIdx.x; kt < n_kv_max; kt += blockDim.x) {
+        uint8_t cls = 3;
+        if (kt < m.nkt) cls = !(c[kt] & 1u) ? 0 : ((c[kt] >> 8) == 0xFFu ? 2 : 1);
+        out[kt] = cls;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------
 
@@ -1589,7 +1781,44 @@ fa_kargs make_kargs(const fa_plan& p, const void* q, const void* k, const void* 
     a.block_size = p.block_size;
     a.log2_block_size = p.log2_block_size;
     a.num_pages = p.num_pages;
+    if (p.dense_tiles && p.ws_bytes > 0) {
+        char* ws = static_cast<char*>(workspace);
+        a.tile_list = reinterpret_cast<const uint32_t*>(ws + p.ws_list_offset);
+        a.tile_bits = reinterpret_cast<const uint32_t*>(ws + p.ws_bits_offset);
+        a.dense_nqt = p.dense_nqt;
+        a.dense_nkt = p.dense_nkt;
+        a.m_heads = p.mask_heads;
+        a.m_bcast_b = p.m_bcast_b;
+        a.m_bcast_h = p.m_bcast_h;
+    }
     return a;
+}
+
+fa_mask_args make_mask_args(const fa_plan& p, const uint8_t* mask, void* workspace) {
+    fa_mask_args m{};
+    char* ws = static_cast<char*>(workspace);
+    m.mask = mask;
+    m.m_bs = p.m_bs;
+    m.m_hs = p.m_hs;
+    m.m_rs = p.m_rs;
+    m.sq = p.geom0.sq;
+    m.skv = p.geom0.skv;
+    m.nqt = p.dense_nqt;
+    m.nkt = p.dense_nkt;
+    m.m_heads = p.mask_heads;
+    m.cls = reinterpret_cast<uint16_t*>(ws + p.ws_cls_offset);
+    m.lists = reinterpret_cast<uint32_t*>(ws + p.ws_list_offset);
+    m.bits = reinterpret_cast<uint32_t*>(ws + p.ws_bits_offset);
+    return m;
+}
+
+// The dense-mask pre-pass (classify, then list). with_lists = false: classes and bits only.
+void launch_mask_prepass(const fa_mask_args& m, int slices, bool with_lists, hipStream_t s) {
+    const bool aligned = (m.skv % 16) == 0 && (reinterpret_cast<uintptr_t>(m.mask) % 16) == 0;
+    const dim3 grid(unsigned((m.nkt + MC_TILES - 1) / MC_TILES), unsigned(m.nqt), unsigned(slices));
+    if (aligned) fa_mask_classify<true><<<grid, dim3(256), 0, s>>>(m);
+    else fa_mask_classify<false><<<grid, dim3(256), 0, s>>>(m);
+    if (with_lists) fa_mask_compact<<<dim3(unsigned(m.nqt), unsigned(slices)), dim3(64), 0, s>>>(m);
 }
 
 bool log_enabled() {
@@ -1695,6 +1924,11 @@ fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v,
     }
     st = upload_tables(p, workspace, s);
     if (st != FA_OK) return st;
+    if (p.dense_tiles && p.ws_bytes > 0) {
+        (void)hipGetLastError();
+        launch_mask_prepass(make_mask_args(p, atten_mask, workspace), p.mask_slices, true, s);
+        if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    }
     fa_kargs a = make_kargs(p, q, k, v, out, softmax_lse, alibi_slopes, atten_mask, workspace, c.scale);
     a.alibi_left = c.alibi_mode == FA_ALIBI_LEFT ? 1 : 0;
     a.block_table = p.paged ? block_table : nullptr;
@@ -1928,7 +2162,8 @@ extern "C" fa_status fa_mask_probe(const fa_dims* dims, int32_t layout, int32_t 
     fa_plan p;
     fa_status st = fa_make_plan(c, true, &p);
     if (st != FA_OK) return st;
-    if (sparse_mode == 1 && tile_class) return FA_ERR_PARAM_INVALID;
+    // Mode 1 has a tile map where the forward runs the dense-mask pre-pass.
+    if (sparse_mode == 1 && tile_class && !p.dense_tiles) return FA_ERR_UNSUPPORTED;
     if (!p.empty && !row_visible_counts) return FA_ERR_NULLPTR;
     if (p.ws_bytes > 0) {
         if (!workspace) return FA_ERR_NULLPTR;
@@ -1942,7 +2177,14 @@ extern "C" fa_status fa_mask_probe(const fa_dims* dims, int32_t layout, int32_t 
                                   workspace, 1.0f);
     (void)hipGetLastError();
     fa_probe_rows<<<dim3(p.B, p.N), dim3(256), 0, s>>>(a, row_visible_counts, sparse_mode == 1);
-    if (tile_class && p.n_kvtiles_max > 0) {
+    if (sparse_mode == 1) {
+        if (tile_class && p.ws_bytes > 0 && p.dense_nqt > 0) {
+            const fa_mask_args m = make_mask_args(p, atten_mask, workspace);
+            launch_mask_prepass(m, p.mask_slices, false, s);
+            fa_probe_tiles_dense<<<dim3(unsigned(p.dense_nqt), unsigned(p.N), unsigned(p.B)), dim3(256), 0, s>>>(
+                m, tile_class, p.n_kvtiles_max, p.N, p.m_bcast_b, p.m_bcast_h);
+        }
+    } else if (tile_class && p.n_kvtiles_max > 0) {
         int64_t max_nqt = 0;
         for (const fa_geom& g : p.geoms) max_nqt = std::max<int64_t>(max_nqt, (g.sq + p.bm - 1) / p.bm);
         if (max_nqt > 0)

@@ -296,6 +296,16 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         p.m_rs = d.Skv;
         p.m_hs = hb ? 0 : d.Sq * d.Skv;
         p.m_bs = bb ? 0 : nm * d.Sq * d.Skv;
+        if (p.kernel == FA_KERNEL_PP && !tnd) {
+            // The ping-pong kernel visits only the kv tiles the pre-pass found a visible entry in.
+            p.dense_tiles = true;
+            p.m_bcast_b = bb ? 1 : 0;
+            p.m_bcast_h = hb ? 1 : 0;
+            p.mask_heads = int32_t(nm);
+            p.mask_slices = int32_t((bb ? 1 : B) * nm);
+            p.dense_nqt = int32_t(ceil_div(d.Sq, FA_PP_BM));
+            p.dense_nkt = int32_t(ceil_div(d.Skv, FA_PP_BN));
+        }
     }
 
     // Work items.
@@ -460,6 +470,9 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         p.n_qtiles_fixed = int32_t(ceil_div(d.Sq, p.bm));
         p.n_items = B * p.n_qtiles_fixed;
         p.ws_bytes = 0;
+        if (p.dense_tiles && !p.empty && d.Skv > 0)
+            p.ws_bytes = fa_dense_ws_layout(p.mask_slices, p.dense_nqt, p.dense_nkt, &p.ws_cls_offset,
+                                            &p.ws_list_offset, &p.ws_bits_offset);
         if (B > 0 && p.n_qtiles_fixed > 1 && !sizes_only)
             p.reverse_qt = item_cost(0, p.n_qtiles_fixed - 1, nullptr) > item_cost(0, 0, nullptr);
         const char* xm = std::getenv("FA_XCD_MAJOR");
@@ -513,6 +526,15 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
     return FA_OK;
 }
 
+size_t fa_dense_ws_layout(int64_t slices, int64_t nqt, int64_t nkt, size_t* cls_off, size_t* list_off,
+                          size_t* bits_off) {
+    const size_t tiles = size_t(slices) * size_t(nqt) * size_t(nkt);
+    *cls_off = 0;
+    *list_off = align256(tiles * sizeof(uint16_t));
+    *bits_off = align256(*list_off + size_t(slices) * size_t(nqt) * size_t(nkt + 1) * sizeof(uint32_t));
+    return align256(*bits_off + tiles * 512 * sizeof(uint32_t));
+}
+
 fa_status fa_make_plan(const fa_call& call, bool with_tables, fa_plan* plan) {
     return make_plan_impl(call, with_tables, false, plan);
 }
@@ -547,6 +569,21 @@ extern "C" fa_status fa_fwd_workspace_size(const fa_dims* dims, int32_t layout,
     c.sparse_mode = sparse_mode;
     c.actual_seq_qlen = actual_seq_qlen;
     c.actual_seq_kvlen = actual_seq_kvlen;
+    fa_plan p;
+    const fa_status st = fa_make_plan_sizes(c, &p);
+    if (st != FA_OK) return st;
+    *bytes = p.ws_bytes;
+    return FA_OK;
+}
+
+extern "C" fa_status fa_fwd_mask_workspace_size(const fa_dims* dims, int32_t layout,
+                                                const int64_t* mask_bcast, size_t* bytes) {
+    if (!dims || !bytes) return FA_ERR_NULLPTR;
+    fa_call c;
+    c.dims = dims;
+    c.layout = layout;
+    c.sparse_mode = 1;
+    c.mask_bcast = mask_bcast;
     fa_plan p;
     const fa_status st = fa_make_plan_sizes(c, &p);
     if (st != FA_OK) return st;

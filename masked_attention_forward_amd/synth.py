@@ -100,6 +100,17 @@ class Workload:
     def slopes(self):
         return alibi_slopes(self.N) if self.alibi else None
 
+    def mask(self):
+        """(atten_mask, mask_bcast) of a sparse_mode=1 workload, else (None, None).
+
+        "upper_triangle": one uint8 [1, 1, Sq, Skv] tensor shared by every batch and head, 1
+        (masked) where j - i > Skv - Sq: the rightDownCausal pattern handed over as an explicit
+        mask."""
+        if self.extra.get("mask") == "upper_triangle":
+            m = torch.ones(self.Sq, self.Skv, dtype=torch.uint8).triu(1 + self.Skv - self.Sq)
+            return m[None, None].contiguous(), [1, 1]
+        return None, None
+
 
 NO_MASK = 2 ** 62   # a pre/next value that reaches past any sequence: "no mask" in mode 0
 
@@ -142,6 +153,10 @@ def workloads() -> dict:
                                   sparse_mode=0, pre_tokens=1024, next_tokens=-256, seed=32)
     w["causal_8192"] = Workload("causal_8192", "BNSD", "bf16", 2, 32, 128, 8192, 8192,
                                 sparse_mode=3, seed=8)
+    # The headline's shape and inputs with sparseMode=1: the same causal pattern, read from an
+    # explicit uint8 mask shared by every batch and head.
+    w["causal_8192_mask"] = Workload("causal_8192_mask", "BNSD", "bf16", 2, 32, 128, 8192, 8192,
+                                     sparse_mode=1, seed=8, extra={"mask": "upper_triangle"})
     lens = lengths_uniform(16, 128, 4096, seed=4)
     w["varlen_tnd"] = Workload("varlen_tnd", "TND", "bf16", 16, 32, 128, qlens=lens,
                                kvlens=list(lens), sparse_mode=3, seed=4)

@@ -517,7 +517,7 @@ def _slice_of(o, lse, w, b, h):
 
 
 @pytest.mark.parametrize("name", ["causal_2048", "band_8192", "band_neg_8192", "causal_8192",
-                                  "varlen_tnd", "prefix_alibi", "prefix_alibi_square"])
+                                  "varlen_tnd", "prefix_alibi", "prefix_alibi_square", "causal_8192_mask"])
 def test_config_full_size(gpu_device, name):
     """Each full-size workload, run once in the launch configuration bench.py times, against
     the oracle: whole (batch, head) slices element by element (all 64 of the headline, 8 of
@@ -526,7 +526,9 @@ def test_config_full_size(gpu_device, name):
     q, k, v = w.tensors()
     kw = dict(pre_tokens=w.pre_tokens, next_tokens=w.next_tokens, prefix=w.prefix,
               actual_seq_qlen=w.actual_seq_qlen, actual_seq_kvlen=w.actual_seq_kvlen)
-    o, lse = run(q, k, v, w.layout, w.sparse_mode, w.softmax_scale, gpu_device, slopes=w.slopes(), **kw)
+    mask, bcast = w.mask()
+    o, lse = run(q, k, v, w.layout, w.sparse_mode, w.softmax_scale, gpu_device, slopes=w.slopes(),
+                 mask=None if mask is None else mask.numpy(), mask_bcast=bcast, **kw)
     assert torch.isfinite(o).all()
     assert not torch.isnan(lse).any()
     qn, kn, vn = (x.float().numpy() for x in (q, k, v))
@@ -535,6 +537,8 @@ def test_config_full_size(gpu_device, name):
     print(f"[full] {name}: {len(slices)} whole slices", flush=True)
     for b, h in slices:
         qs, ks, vs, okw = _slice_problem(w, qn, kn, vn, b, h)
+        if mask is not None:
+            okw["atten_mask"] = mask.numpy()   # [1, 1, Sq, Skv]: the same for every slice
         ref_o, ref_l = ref_attention(qs.astype(np.float64), ks.astype(np.float64), vs.astype(np.float64), **okw)
         got_o, got_l = _slice_of(on, ln, w, b, h)
         ref_o = ref_o.reshape(got_o.shape)
@@ -545,7 +549,7 @@ def test_config_full_size(gpu_device, name):
     rows = _sample_rows(w, rng)
     ref_o, ref_l = oracle.attention_rows(qn, kn, vn, rows, layout=w.layout, sparse_mode=w.sparse_mode,
                                          scale=f32_exact(w.softmax_scale), alibi_slopes=f32_exact(w.slopes()),
-                                         **kw)
+                                         atten_mask=None if mask is None else mask.numpy(), **kw)
     got_o, got_l = _gather(o, lse, w, rows)
     check(torch.from_numpy(got_o), torch.from_numpy(got_l), ref_o, ref_l, DT[w.dtype], f"{name} sampled rows")
 
@@ -587,3 +591,89 @@ def test_single_key_rows_return_value(gpu_device):
     assert torch.equal(o, v)
     ref = 0.1 * (to64(q) * to64(k)).sum(-1)
     assert np.abs(lse.double().numpy() - ref).max() < 1e-4
+
+
+# ---------------------------------------------------------------------------------------
+# Dense mask (sparseMode=1): the pre-pass tile map and the tile-skipping kernel path
+# ---------------------------------------------------------------------------------------
+
+def structured_mask(rng, mb, mh, sq, skv):
+    """A uint8 mask (1 = masked) with structure at the kernel's tile scale: 32-row x 64-key
+    blocks that are fully masked, fully visible or random; in every other slice the region on
+    and below the bottom-right diagonal opened to 90% visible; fully masked rows; and a whole
+    256-row q tile with nothing visible. Every tile class and the empty work item occur."""
+    m = np.ones((mb, mh, sq, skv), dtype=np.uint8)
+    for b in range(mb):
+        for h in range(mh):
+            for r0 in range(0, sq, 32):
+                for c0 in range(0, skv, 64):
+                    kind = rng.integers(0, 4)
+                    blk = m[b, h, r0:r0 + 32, c0:c0 + 64]
+                    if kind == 1:
+                        blk[...] = 0
+                    elif kind == 2:
+                        blk[...] = (rng.random(blk.shape) < 0.5)
+            i = np.arange(sq)[:, None]
+            j = np.arange(skv)[None, :]
+            causal = (j <= i + (skv - sq))
+            if (b + h) % 2 == 0:
+                m[b, h] &= ~causal.astype(bool) | (rng.random((sq, skv)) < 0.1)
+            m[b, h, 7, :] = 1                 # a row that sees nothing
+            if sq > 300:
+                m[b, h, 256:512, :] = 1       # a q tile with nothing visible
+    return m
+
+
+@pytest.mark.parametrize("bcast", [[0, 0], [1, 0], [0, 1], [1, 1]])
+def test_probe_dense_mask_tiles(gpu_device, bcast):
+    """Mode-1 tile classes (from the pre-pass the forward runs) against brute force over the
+    mask, bit-exact, for aligned (Skv % 16 == 0) and unaligned mask rows."""
+    rng = np.random.default_rng(2100 + 2 * bcast[0] + bcast[1])
+    B, N = 2, 3
+    for sq, skv in [(600, 704), (300, 333), (5, 70)]:
+        mb, mh = (1 if bcast[0] else B), (1 if bcast[1] else N)
+        mask = structured_mask(rng, mb, mh, sq, skv)
+        dims = fb.make_dims(torch.bfloat16, 0, B=B, N=N, Sq=sq, Skv=skv, D=128)
+        print(f"[probe-dense] sq={sq} skv={skv} bcast={bcast}", flush=True)
+        counts, tiles = fb.fa_mask_probe(dims, "BNSD", 1, device=gpu_device,
+                                         atten_mask=torch.from_numpy(mask).to(gpu_device), mask_bcast=bcast)
+        torch.cuda.synchronize()
+        bm, bn, nq, nk = fb.fa_tile_shape(dims, "BNSD")
+        exp = []
+        for b in range(B):
+            for h in range(N):
+                vis = mask[0 if bcast[0] else b, 0 if bcast[1] else h] == 0
+                assert counts[b, h].cpu().numpy().tolist() == vis.sum(axis=1).tolist()
+                exp += brute_class(vis, bm, bn, nk)
+        assert tiles.cpu().numpy().tolist() == exp
+
+
+@pytest.mark.parametrize("bcast", [[0, 0], [1, 1], [0, 1]])
+def test_parity_dense_mask_tiles(gpu_device, bcast):
+    """Mode 1 on the MFMA kernel with masks whose tiles are skipped, fully visible or partial,
+    empty rows and an empty q tile, against the oracle (bf16 D 128, fp16 D 64; aligned and
+    unaligned mask rows; with and without alibi)."""
+    rng = np.random.default_rng(2200 + 2 * bcast[0] + bcast[1])
+    for dtype, D, layout in [("bf16", 128, "BNSD"), ("f16", 64, "BSND")]:
+        for sq, skv in [(600, 704), (300, 333)]:
+            B, N = 2, 3
+            mb, mh = (1 if bcast[0] else B), (1 if bcast[1] else N)
+            mask = structured_mask(rng, mb, mh, sq, skv)
+            q, k, v = make_inputs(layout, dtype, B, N, sq, skv, D, seed=2300 + sq)
+            for slopes in (None, [0.3, 0.1, 0.02]):
+                o, lse = run(q, k, v, layout, 1, 0.1, gpu_device, slopes=slopes, mask=mask, mask_bcast=bcast)
+                ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout=layout, sparse_mode=1, scale=0.1,
+                                               atten_mask=mask, alibi_slopes=slopes)
+                check(o, lse, ref_o, ref_lse, DT[dtype], f"mode=1 tiles {dtype} {layout} {sq}x{skv} bcast={bcast}")
+                zero_rows_ok(o, lse, layout)
+
+
+def test_dense_mask_equals_causal_mode(gpu_device):
+    """"sparseMode介绍": mode 1 fed the boolean mask of mode 3 is mode 3. The MFMA kernel visits
+    the same tiles either way, so the results are bitwise equal."""
+    for sq, skv in [(700, 700), (333, 600)]:
+        q, k, v = make_inputs("BNSD", "bf16", 2, 4, sq, skv, 128, seed=2400 + sq)
+        mask = np.triu(np.ones((sq, skv), dtype=np.uint8), 1 + skv - sq)[None, None]
+        o1, l1 = run(q, k, v, "BNSD", 1, 0.088, gpu_device, mask=mask, mask_bcast=[1, 1])
+        o3, l3 = run(q, k, v, "BNSD", 3, 0.088, gpu_device)
+        assert torch.equal(o1, o3) and torch.equal(l1, l3)
