@@ -618,7 +618,7 @@ def structured_mask(rng, mb, mh, sq, skv):
             causal = (j <= i + (skv - sq))
             if (b + h) % 2 == 0:
                 m[b, h] &= ~causal.astype(bool) | (rng.random((sq, skv)) < 0.1)
-            m[b, h, 7, :] = 1                 # a row that sees nothing
+            m[b, h, min(7, sq - 1), :] = 1    # a row that sees nothing
             if sq > 300:
                 m[b, h, 256:512, :] = 1       # a q tile with nothing visible
     return m
