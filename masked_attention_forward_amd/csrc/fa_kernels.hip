@@ -81,6 +81,7 @@ struct fa_kargs {
     // Dense mask (sparse mode 1) on the ping-pong kernel: the pre-pass's tables (workspace).
     const uint32_t* tile_list;    // [slices, nqt, 1 + nkt]: count, then kt | full-wave bits << 24
     const uint32_t* tile_bits;    // [slices, nqt, nkt, 512]: hidden-key bits, one dword per lane
+    const int32_t* tile_perm;     // [slices, nqt]: q tiles of a slice in launch order
     int32_t dense_nqt, dense_nkt;
     int32_t m_heads, m_bcast_b, m_bcast_h;
 };
@@ -579,6 +580,13 @@ fa_fwd_pp(const fa_kargs a) {
     int b, h, qt;
     fa_geom g;
     fa_decode_item(a, b, h, qt, g);
+    // Dense mask: the q tile of launch rank qt is the pre-pass's choice (most visited tiles first;
+    // a dense mask has no reverse order, so the rank is qt itself).
+    int ms = 0;
+    if constexpr (DENSE) {
+        ms = (a.m_bcast_b ? 0 : b) * a.m_heads + (a.m_bcast_h ? 0 : h);
+        if (a.tile_perm) qt = fa_uniform(a.tile_perm[int64_t(ms) * a.dense_nqt + qt]);
+    }
     const int i0 = qt * BM;
     const int i_last = min(i0 + BM, g.sq) - 1;
     const fa_kv_range kr = fa_tile_kv_range(g, i0, i_last, BN);
@@ -595,7 +603,6 @@ fa_fwd_pp(const fa_kargs a) {
         n_tiles = 0;
         kv_lim = g.skv;
         if (a.tile_list) {
-            const int ms = (a.m_bcast_b ? 0 : b) * a.m_heads + (a.m_bcast_h ? 0 : h);
             const int64_t r = int64_t(ms) * a.dense_nqt + qt;
             trec = (const __attribute__((address_space(4))) uint32_t*)(a.tile_list + r * (a.dense_nkt + 1));
             tbits = a.tile_bits + r * a.dense_nkt * 512 + wave * 64 + lane;
@@ -1631,6 +1638,7 @@ struct fa_mask_args {
     uint16_t* cls;              // [slices, nqt, nkt]: bit 0 any visible, bits 8-15 full per block
     uint32_t* lists;            // [slices, nqt, 1 + nkt]: count, then kt | full bits << 24
     uint32_t* bits;             // [slices, nqt, nkt, 512]
+    int32_t* perm;              // [slices, nqt]: q tiles in launch order (most visited tiles first)
 };
 
 constexpr int MC_TILES = 4;   // kv tiles per classify workgroup
@@ -1731,6 +1739,29 @@ __global__ __launch_bounds__(64) void fa_mask_compact(const fa_mask_args m) {
     if (lane == 0) rec[0] = uint32_t(base);
 }
 
+// Launch order of each slice's q tiles: most visited kv tiles first (ties by q tile), so the
+// longest work items start first and the short ones fill the end. One workgroup per slice ranks
+// every q tile against the others; past FA_ORDER_MAX q tiles the order stays the identity.
+constexpr int FA_ORDER_MAX = 4096;
+
+__global__ __launch_bounds__(256) void fa_mask_order(const fa_mask_args m) {
+    __shared__ uint32_t cnt[FA_ORDER_MAX];
+    const int ms = blockIdx.x;
+    int32_t* perm = m.perm + int64_t(ms) * m.nqt;
+    if (m.nqt > FA_ORDER_MAX) {
+        for (int i = threadIdx.x; i < m.nqt; i += blockDim.x) perm[i] = i;
+        return;
+    }
+    for (int i = threadIdx.x; i < m.nqt; i += blockDim.x) cnt[i] = m.lists[(int64_t(ms) * m.nqt + i) * (m.nkt + 1)];
+    __syncthreads();
+    for (int i = threadIdx.x; i < m.nqt; i += blockDim.x) {
+        const uint32_t c = cnt[i];
+        int rank = 0;
+        for (int j = 0; j < m.nqt; ++j) rank += (cnt[j] > c || (cnt[j] == c && j < i)) ? 1 : 0;
+        perm[rank] = i;
+    }
+}
+
 // Mask probe of mode 1: tile classes of every (batch, head, q tile) from the pre-pass.
 __global__ void fa_probe_tiles_dense(const fa_mask_args m, uint8_t* tile_class, int64_t n_kv_max, int N,
                                      int bcast_b, int bcast_h) {
@@ -1785,6 +1816,7 @@ fa_kargs make_kargs(const fa_plan& p, const void* q, const void* k, const void* 
         char* ws = static_cast<char*>(workspace);
         a.tile_list = reinterpret_cast<const uint32_t*>(ws + p.ws_list_offset);
         a.tile_bits = reinterpret_cast<const uint32_t*>(ws + p.ws_bits_offset);
+        a.tile_perm = reinterpret_cast<const int32_t*>(ws + p.ws_perm_offset);
         a.dense_nqt = p.dense_nqt;
         a.dense_nkt = p.dense_nkt;
         a.m_heads = p.mask_heads;
@@ -1809,6 +1841,7 @@ fa_mask_args make_mask_args(const fa_plan& p, const uint8_t* mask, void* workspa
     m.cls = reinterpret_cast<uint16_t*>(ws + p.ws_cls_offset);
     m.lists = reinterpret_cast<uint32_t*>(ws + p.ws_list_offset);
     m.bits = reinterpret_cast<uint32_t*>(ws + p.ws_bits_offset);
+    m.perm = reinterpret_cast<int32_t*>(ws + p.ws_perm_offset);
     return m;
 }
 
@@ -1818,7 +1851,10 @@ void launch_mask_prepass(const fa_mask_args& m, int slices, bool with_lists, hip
     const dim3 grid(unsigned((m.nkt + MC_TILES - 1) / MC_TILES), unsigned(m.nqt), unsigned(slices));
     if (aligned) fa_mask_classify<true><<<grid, dim3(256), 0, s>>>(m);
     else fa_mask_classify<false><<<grid, dim3(256), 0, s>>>(m);
-    if (with_lists) fa_mask_compact<<<dim3(unsigned(m.nqt), unsigned(slices)), dim3(64), 0, s>>>(m);
+    if (with_lists) {
+        fa_mask_compact<<<dim3(unsigned(m.nqt), unsigned(slices)), dim3(64), 0, s>>>(m);
+        fa_mask_order<<<dim3(unsigned(slices)), dim3(256), 0, s>>>(m);
+    }
 }
 
 bool log_enabled() {

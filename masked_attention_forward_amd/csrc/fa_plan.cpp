@@ -472,7 +472,7 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         p.ws_bytes = 0;
         if (p.dense_tiles && !p.empty && d.Skv > 0)
             p.ws_bytes = fa_dense_ws_layout(p.mask_slices, p.dense_nqt, p.dense_nkt, &p.ws_cls_offset,
-                                            &p.ws_list_offset, &p.ws_bits_offset);
+                                            &p.ws_list_offset, &p.ws_bits_offset, &p.ws_perm_offset);
         if (B > 0 && p.n_qtiles_fixed > 1 && !sizes_only)
             p.reverse_qt = item_cost(0, p.n_qtiles_fixed - 1, nullptr) > item_cost(0, 0, nullptr);
         const char* xm = std::getenv("FA_XCD_MAJOR");
@@ -527,12 +527,13 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
 }
 
 size_t fa_dense_ws_layout(int64_t slices, int64_t nqt, int64_t nkt, size_t* cls_off, size_t* list_off,
-                          size_t* bits_off) {
+                          size_t* bits_off, size_t* perm_off) {
     const size_t tiles = size_t(slices) * size_t(nqt) * size_t(nkt);
     *cls_off = 0;
     *list_off = align256(tiles * sizeof(uint16_t));
     *bits_off = align256(*list_off + size_t(slices) * size_t(nqt) * size_t(nkt + 1) * sizeof(uint32_t));
-    return align256(*bits_off + tiles * 512 * sizeof(uint32_t));
+    *perm_off = align256(*bits_off + tiles * 512 * sizeof(uint32_t));
+    return align256(*perm_off + size_t(slices) * size_t(nqt) * sizeof(int32_t));
 }
 
 fa_status fa_make_plan(const fa_call& call, bool with_tables, fa_plan* plan) {

@@ -106,7 +106,7 @@ struct fa_plan {
     int32_t mask_slices = 0, mask_heads = 0;    // slices = (B or 1) x (N or 1); heads = N or 1
     int32_t m_bcast_b = 0, m_bcast_h = 0;
     int32_t dense_nqt = 0, dense_nkt = 0;       // q tiles (256 rows) and kv tiles (64 keys) per slice
-    size_t ws_cls_offset = 0, ws_list_offset = 0, ws_bits_offset = 0;
+    size_t ws_cls_offset = 0, ws_list_offset = 0, ws_bits_offset = 0, ws_perm_offset = 0;
     // Statistics (per head).
     int64_t kv_tiles_visited = 0, kv_tiles_full = 0, kv_tiles_total = 0;
 };
@@ -122,10 +122,10 @@ fa_status fa_make_plan_sizes(const fa_call& call, fa_plan* plan);
 
 // Bytes of the mode-1 pre-pass tables for `slices` mask slices of nqt x nkt tiles, and their
 // offsets from the start of the workspace: the tile classes (uint16), the per-q-tile lists
-// (count, then one uint32 entry per visited tile) and the packed mask bits (512 uint32 per
-// tile).
+// (count, then one uint32 entry per visited tile), the packed mask bits (512 uint32 per tile)
+// and each slice's q tiles in launch order (int32, most visited tiles first).
 size_t fa_dense_ws_layout(int64_t slices, int64_t nqt, int64_t nkt, size_t* cls_off, size_t* list_off,
-                          size_t* bits_off);
+                          size_t* bits_off, size_t* perm_off);
 
 // Serialises the per-batch geometry and work items into a host image of the leading
 // ws_table_bytes of the workspace.
