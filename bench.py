@@ -33,6 +33,8 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 flop
 PEAK_HBM_GBS = 8000.0
 # Sources that decide the dominant kernel's memory traffic (its code and its launch order).
 KERNEL_SOURCES = ["masked_attention_forward_amd/csrc/fa_kernels.hip",
+                  "masked_attention_forward_amd/csrc/fa_fwd_ps.hip",
+                  "masked_attention_forward_amd/csrc/fa_fwd_common.h",
                   "masked_attention_forward_amd/csrc/fa_mask.h",
                   "masked_attention_forward_amd/csrc/fa_plan.cpp",
                   "masked_attention_forward_amd/csrc/fa_plan.h"]

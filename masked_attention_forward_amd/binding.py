@@ -59,7 +59,7 @@ _LIB = None
 
 
 def library_path() -> str:
-    return os.environ.get("FA_LIBRARY", os.path.join(HERE, "lib", "libfa.so"))
+    return os.environ.get("FA_LIBRARY") or os.path.join(HERE, "lib", "libfa.so")
 
 
 def load_library():

@@ -45,125 +45,15 @@
 #include <vector>
 
 #include "fa_device.h"
+#include "fa_fwd_common.h"
 #include "fa_mask.h"
 #include "fa_plan.h"
 
 namespace {
 
-struct fa_kargs {
-    const void* q;
-    const void* k;
-    const void* v;
-    void* o;
-    float* lse;
-    const float* slopes;
-    const uint8_t* mask;
-    const fa_geom* geoms;   // per-batch table (workspace) or nullptr
-    const int32_t* items;   // (b, q tile) launch list (workspace) or nullptr
-    fa_geom geom0;          // shared geometry when there is no table
-    int64_t q_bs, q_hs, q_rs;
-    int64_t kv_bs, kv_hs, kv_rs;
-    int64_t lse_bs, lse_hs;
-    int64_t m_bs, m_hs, m_rs;
-    int32_t B, N, D;
-    int32_t n_qtiles_fixed;
-    int32_t reverse_qt;
-    int32_t xcd_major;      // fixed-length launch order, see fa_decode_item
-    int32_t alibi_left;     // linear alibi measured from the top-left diagonal (else bottom-right)
-    float scale_log2;       // scale * log2(e)
-    // Paged K / V (k and v are the caches; kv_bs = 0, sequences start at key 0 of their pages).
-    const int32_t* block_table;   // [B, bt_stride] page ids, or nullptr
-    int64_t page_stride;          // elements from one page to the next
-    int64_t bt_stride;
-    int32_t block_size;
-    int32_t log2_block_size;      // ping-pong kernel: block_size = 2^log2_block_size >= 64
-    int32_t num_pages;            // valid page ids are [0, num_pages)
-    // Dense mask (sparse mode 1) on the ping-pong kernel: the pre-pass's tables (workspace).
-    const uint32_t* tile_list;    // [slices, nqt, 1 + nkt]: count, then kt | full-wave bits << 24
-    const uint32_t* tile_bits;    // [slices, nqt, nkt, 512]: hidden-key bits, one dword per lane
-    const int32_t* tile_perm;     // [slices, nqt]: q tiles of a slice in launch order
-    int32_t dense_nqt, dense_nkt;
-    int32_t m_heads, m_bcast_b, m_bcast_h;
-};
-
-// Work item of this workgroup. Workgroups are dispatched round-robin over the 8 XCDs, each
-// with its own L2. Table mode (varlen / prefix): heads are the fastest index, so the blocks
-// of one (batch, head) share an XCD when N is a multiple of 8, and items run heaviest first
-// (the planner sorted the table). Fixed-length mode with xcd_major: XCD x = blockIdx % 8
-// works through the (batch, head) pairs congruent to x one pair at a time, heaviest q tile
-// first, so each XCD streams the K/V of about one pair through its L2 at a time.
-
-__device__ __forceinline__ fa_geom fa_geom_of(const fa_kargs& a, int b) {
-    if (!a.geoms) return a.geom0;
-    const fa_geom t = a.geoms[b];
-    fa_geom g;
-    g.q_start = fa_uniform(t.q_start);
-    g.kv_start = fa_uniform(t.kv_start);
-    g.sq = fa_uniform(t.sq);
-    g.skv = fa_uniform(t.skv);
-    g.a = fa_uniform(t.a);
-    g.c = fa_uniform(t.c);
-    g.f = fa_uniform(t.f);
-    g.pad = 0;
-    return g;
-}
-
-__device__ __forceinline__ void fa_decode_item(const fa_kargs& a, int& b, int& h, int& qt,
-                                               fa_geom& g) {
-    const int w = blockIdx.x;
-    h = w % a.N;
-    const int item = w / a.N;
-    if (a.items) {
-        b = fa_uniform(a.items[2 * item]);
-        qt = fa_uniform(a.items[2 * item + 1]);
-    } else if (a.xcd_major) {
-        // Pair-major (1): the pairs of XCD x one after another, each heaviest q tile first.
-        // Rank-major (2): the heaviest q tile of every pair of XCD x, then the next rank.
-        const int x = w & 7, slot = w >> 3;
-        const int ppx = a.B * a.N / 8;
-        const int pair = (a.xcd_major == 2 ? slot % ppx : slot / a.n_qtiles_fixed) * 8 + x;
-        const int r = a.xcd_major == 2 ? slot / ppx : slot % a.n_qtiles_fixed;
-        b = pair / a.N;
-        h = pair % a.N;
-        qt = a.reverse_qt ? a.n_qtiles_fixed - 1 - r : r;
-    } else {
-        const int r = item / a.B;
-        b = item % a.B;
-        qt = a.reverse_qt ? a.n_qtiles_fixed - 1 - r : r;
-    }
-    g = fa_geom_of(a, b);
-}
-
 // ------------------------------------------------------------------------------------------
 // MFMA kernel
 // ------------------------------------------------------------------------------------------
-
-// max / sum of x over the lane pair (l, l ^ 32); both lanes get the same bits.
-__device__ __forceinline__ float pair_max(float x) {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-
-// K and V tiles live in LDS row-major (a row is D/8 chunks of 16 bytes); chunk c of row j
-// sits at c ^ swz(j). D = 128 (256-byte rows): swz swaps the two 2-bit fields of j & 15, a
-// bijection, so the 16 rows one 16-lane group reads with ds_read_b128 (K) land on 16
-// distinct bank groups; and 4 consecutive rows (j & 3 = 0..3) XOR chunk bits 2-3 with
-// distinct values, so the 4 rows x 4 chunks that lanes 0-31 touch with a V transpose read
-// cover all 16 bank groups once. D = 64 (two 128-byte rows per 256-byte line): the same
-// idea on y = j >> 1.
-template <int KCH>
-__device__ __forceinline__ int fa_swz(int j, int c) {
-    if constexpr (KCH == 16) return c ^ (((j & 3) << 2) | ((j >> 2) & 3));
-    else {
-        const int y = j >> 1;
-        return c ^ (((y & 1) << 2) | ((y >> 1) & 3));
-    }
-}
 
 constexpr int MF_BM = FA_MFMA32_BM;   // 128 query rows per workgroup (4 waves x 32 rows)
 constexpr int MF_BN = FA_MFMA32_BN;   // 64 keys per kv tile
@@ -513,41 +403,6 @@ fa_fwd_mfma(const fa_kargs a) {
 // u + 2 becomes writable and waits for them (vmcnt) at the end of the following phase.
 // Phase barriers order LDS only, so loads stay in flight across them.
 // ------------------------------------------------------------------------------------------
-
-// Dense-mask tile entries: the kv tile index in the low 24 bits; FA_DENSE_END (past the list)
-// names a tile past every key, whose loads read nothing.
-constexpr uint32_t FA_DENSE_KT = 0xFFFFFFu;
-constexpr uint32_t FA_DENSE_END = 0xFFFFFFFFu;
-
-constexpr int PP_BM = FA_PP_BM;   // 256 query rows per workgroup (8 waves x 32 rows)
-constexpr int PP_BN = FA_PP_BN;   // 64 keys per kv tile
-constexpr int PP_THREADS = 512;
-
-// Phase barrier: waits for this wave's LDS reads (lgkmcnt 0) but not for its direct-to-LDS
-// loads (vmcnt), which are waited for explicitly in the phase before their data is read; a
-// memory fence here would wait for those loads too. The empty asm statements keep the
-// compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void fa_lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left alone
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Phase barrier that lets this wave's last N LDS reads stay in flight (LDS operations complete
-// in order, so everything issued before them has completed). For reads of data that no other
-// wave overwrites before the next barrier.
-template <int N>
-__device__ __forceinline__ void fa_lds_barrier_pending() {
-    static_assert(N >= 0 && N < 16, "lgkmcnt range");
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));   // lgkmcnt(N); vmcnt and expcnt left alone
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt immediate for vmcnt(n) alone (n < 16).
-constexpr int fa_vmcnt(int n) { return 0x0F70 | n; }
 
 template <int D, bool IS_BF16, int AL, bool DENSE, bool PAGED = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(PP_THREADS, PP_THREADS),
@@ -1857,6 +1712,61 @@ void launch_mask_prepass(const fa_mask_args& m, int slices, bool with_lists, hip
     }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// FA_PERSIST=1 runs the persistent kernel for the ping-pong kernel's problems without a dense
+// mask or paged K/V.
+bool persist_enabled() {
+    const char* e = std::getenv("FA_PERSIST");
+    return e && e[0] == '1';
+}
+
+// The persistent schedule (fa_fwd_ps.hip): one workgroup per compute unit, lists per XCD when
+// the (batch, head) pairs split evenly over the 8 XCDs. Returns the grid size (0: not used).
+unsigned persistent_schedule(const fa_plan& p, fa_ps_args* ps) {
+    int cus = device_cus();
+    if (cus < 8) return 0;
+    // FA_PS_SLOTS: workgroups per launch instead of the compute unit count (comparisons).
+    if (const char* e = std::getenv("FA_PS_SLOTS")) cus = std::max(8, std::atoi(e));
+    *ps = fa_ps_args{};
+    const int64_t pairs = int64_t(p.B) * p.N;
+    ps->N = p.N;
+    ps->reverse_qt = p.reverse_qt;
+    ps->table = p.table ? 1 : 0;
+    fa_magic_divisor(uint32_t(p.N), &ps->n_mul, &ps->n_shr);
+    unsigned grid;
+    if (!p.table && p.xcd_major) {
+        ps->xcd = 1;
+        ps->nq = p.n_qtiles_fixed;
+        const int64_t n_list = pairs / 8 * p.n_qtiles_fixed;
+        if (n_list >= (int64_t(1) << 31)) return 0;
+        ps->n_list = int32_t(n_list);
+        ps->W = int32_t(std::min<int64_t>(cus / 8, n_list));
+        grid = unsigned(8 * ps->W);
+    } else {
+        ps->xcd = 0;
+        ps->nq = p.table ? 1 : p.n_qtiles_fixed;
+        const int64_t n_list = p.table ? p.n_items * p.N : pairs * p.n_qtiles_fixed;
+        if (n_list >= (int64_t(1) << 31)) return 0;
+        ps->n_list = int32_t(n_list);
+        ps->W = int32_t(std::min<int64_t>(cus, n_list));
+        grid = unsigned(ps->W);
+    }
+    fa_magic_divisor(uint32_t(std::max(ps->nq, 1)), &ps->nq_mul, &ps->nq_shr);
+    return grid;
+}
+
 bool log_enabled() {
     const char* e = std::getenv("FA_LOG");
     return e && e[0] == '1';
@@ -2019,6 +1929,14 @@ fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v,
             if (bf) launch_pp_paged_d<64, true>(a, alibi, grid, s);
             else launch_pp_paged_d<64, false>(a, alibi, grid, s);
         }
+    } else if (p.kernel == FA_KERNEL_PP && !dense && persist_enabled() && [&] {
+                   fa_ps_args ps;
+                   const unsigned g = persistent_schedule(p, &ps);
+                   if (g == 0) return false;
+                   launch_fwd_ps(a, ps, p.D, dtype == FA_DTYPE_BF16, alibi, g, s);
+                   return true;
+               }()) {
+        // launched above
     } else if (p.kernel == FA_KERNEL_PP) {
         const bool bf = dtype == FA_DTYPE_BF16;
         if (p.D == 128) {

@@ -677,3 +677,44 @@ def test_dense_mask_equals_causal_mode(gpu_device):
         o1, l1 = run(q, k, v, "BNSD", 1, 0.088, gpu_device, mask=mask, mask_bcast=[1, 1])
         o3, l3 = run(q, k, v, "BNSD", 3, 0.088, gpu_device)
         assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+@pytest.mark.parametrize("case", ["fixed", "table", "band_empty_items"])
+def test_parity_persistent_kernel(gpu_device, monkeypatch, case):
+    """The persistent kernel (FA_PERSIST=1: one workgroup per compute unit streaming the K/V
+    tiles of several items back to back) against the oracle: fixed-length lists per XCD, the
+    varlen / prefix table, items without any visible key (written as empty), several items per
+    workgroup (FA_PS_SLOTS=8 forces eight workgroups), alibi, and D 64 / 128."""
+    monkeypatch.setenv("FA_PERSIST", "1")
+    monkeypatch.setenv("FA_PS_SLOTS", "8")
+    if case == "fixed":
+        for dtype, D, layout, mode, args in [("bf16", 128, "BNSD", 3, {}), ("f16", 64, "BSND", 4, dict(pre_tokens=70, next_tokens=9)),
+                                             ("bf16", 128, "BNSD", 0, dict(pre_tokens=600, next_tokens=-300))]:
+            q, k, v = make_inputs(layout, dtype, 2, 4, 700, 650, D, seed=3100 + D)
+            for slopes in (None, [0.3, 0.1, 0.02, 0.5]):
+                o, lse = run(q, k, v, layout, mode, 0.09, gpu_device, slopes=slopes, **args)
+                ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout=layout, sparse_mode=mode, scale=0.09,
+                                               alibi_slopes=slopes, **args)
+                check(o, lse, ref_o, ref_lse, DT[dtype], f"persistent {layout} mode={mode} {dtype}")
+                zero_rows_ok(o, lse, layout)
+    elif case == "table":
+        ql, kl = [700, 0, 33, 300, 512, 1], [700, 12, 64, 300, 600, 900]
+        q, k, v = make_inputs("TND", "bf16", len(ql), 4, 0, 0, 128, seed=3200, qlens=ql, kvlens=kl)
+        cq, ck = synth.cumulative_ends(ql), synth.cumulative_ends(kl)
+        o, lse = run(q, k, v, "TND", 3, 0.09, gpu_device, slopes=[0.3, 0.1, 0.02, 0.5], actual_seq_qlen=cq,
+                     actual_seq_kvlen=ck)
+        ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout="TND", sparse_mode=3, scale=0.09,
+                                       alibi_slopes=[0.3, 0.1, 0.02, 0.5], actual_seq_qlen=cq, actual_seq_kvlen=ck)
+        check(o, lse, ref_o, ref_lse, torch.bfloat16, "persistent TND")
+        q, k, v = make_inputs("BNSD", "f16", 2, 4, 600, 700, 64, seed=3201)
+        o, lse = run(q, k, v, "BNSD", 5, 0.1, gpu_device, prefix=[0, 650])
+        ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout="BNSD", sparse_mode=5, scale=0.1, prefix=[0, 650])
+        check(o, lse, ref_o, ref_lse, torch.float16, "persistent prefix")
+    else:
+        # next = -300: the first q tile of each head sees no key, and whole items are empty.
+        q, k, v = make_inputs("BNSD", "bf16", 1, 8, 1100, 1100, 128, seed=3300)
+        o, lse = run(q, k, v, "BNSD", 0, 0.09, gpu_device, pre_tokens=2000, next_tokens=-300)
+        ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout="BNSD", sparse_mode=0, scale=0.09,
+                                       pre_tokens=2000, next_tokens=-300)
+        check(o, lse, ref_o, ref_lse, torch.bfloat16, "persistent empty items")
+        zero_rows_ok(o, lse, "BNSD")
