@@ -150,7 +150,7 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
             if (nxt < 0 && !(pre >= -nxt && -nxt < max_skv)) return FA_ERR_PARAM_INVALID;
             if (pre < 0 && !(nxt >= -pre && -pre < max_sq)) return FA_ERR_PARAM_INVALID;
         }
-        if (mode == 4 && clamp64(pre, -huge, huge) + clamp64(nxt, -huge, huge) < 0)
+        if (mode == 4 && clamp64(pre, -huge, huge) < -clamp64(nxt, -huge, huge))  // pre + next < 0
             return FA_ERR_PARAM_INVALID;
         if (mode == 7) {
             for (int64_t b = 0; b < B; ++b) {
@@ -322,10 +322,17 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         const int32_t i1 = std::min<int32_t>(i0 + p.bm, g.sq) - 1;
         const fa_kv_range r = fa_tile_kv_range(g, i0, i1, p.bn);
         if (full) {
+            // fa_tile_full is the conjunction of one bound on the tile's first column and two
+            // on its last, so the full tiles of a q tile are one contiguous run: find its ends
+            // from both sides. Only the few tiles that a mask edge crosses are partial, so
+            // both scans stop after a handful of steps even for a very long kv range.
             *full = 0;
-            if (mode != 1)
-                for (int32_t kt = r.begin; kt < r.end; ++kt)
-                    *full += fa_tile_full(g, i0, i1, kt * p.bn, p.bn) ? 1 : 0;
+            if (mode != 1) {
+                int32_t lo = r.begin, hi = r.end;
+                while (lo < hi && !fa_tile_full(g, i0, i1, lo * p.bn, p.bn)) ++lo;
+                while (hi > lo && !fa_tile_full(g, i0, i1, (hi - 1) * p.bn, p.bn)) --hi;
+                *full = hi - lo;
+            }
         }
         return r.end - r.begin;
     };
