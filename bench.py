@@ -107,7 +107,10 @@ def recorded_traffic(workload: str, path=None, sources=None, kernel=DOMINANT_KER
         return None
 
 
-def visible_pairs(w, dev) -> int:
+def visible_pairs(w, dev):
+    """(visible (row, key) pairs summed over batches and heads, scores the forward kernel
+    computes): the second is every entry of every tile it visits, from the same device mask
+    code (fa_mask_probe's tile map) and the tile shape the forward plans."""
     import torch
     from masked_attention_forward_amd import binding as fb
 
@@ -118,15 +121,54 @@ def visible_pairs(w, dev) -> int:
     k = torch.empty(qk[1], dtype=synth.DTYPES[w.dtype], device="meta")
     dims = fb.dims_of(q, k, w.layout, w.actual_seq_qlen)
     mask, bcast = w.mask()
-    counts, _ = fb.fa_mask_probe(dims, w.layout, w.sparse_mode, device=dev, pre_tokens=w.pre_tokens,
-                                 next_tokens=w.next_tokens, actual_seq_qlen=w.actual_seq_qlen,
-                                 actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix, tiles=False,
-                                 atten_mask=None if mask is None else mask.to(dev), mask_bcast=bcast)
+    counts, tiles = fb.fa_mask_probe(dims, w.layout, w.sparse_mode, device=dev, pre_tokens=w.pre_tokens,
+                                     next_tokens=w.next_tokens, actual_seq_qlen=w.actual_seq_qlen,
+                                     actual_seq_kvlen=w.actual_seq_kvlen, prefix=w.prefix, tiles=True,
+                                     atten_mask=None if mask is None else mask.to(dev), mask_bcast=bcast)
     total = int(counts.sum().item())
     if w.sparse_mode == 3 and w.layout != "TND" and w.Sq <= w.Skv:
         per_head = w.Sq * (w.Skv - w.Sq) + w.Sq * (w.Sq + 1) // 2
         assert total == per_head * w.B * w.N, (total, per_head)
-    return total
+    bm, bn, _, _ = fb.fa_tile_shape(dims, w.layout, w.actual_seq_qlen, w.actual_seq_kvlen)
+    visited = int(((tiles == 1) | (tiles == 2)).sum().item())
+    # The mode-1 map has a row per (batch, head, q tile); the others one per (batch, q tile).
+    computed = visited * bm * bn * (1 if w.sparse_mode == 1 else w.N)
+    return total, computed
+
+
+def exp2_rate(dev, iters: int = 64, launches: int = 10) -> float:
+    """Measured exp2 throughput of the chip (exponentials per second) from the library's
+    calibration kernel: 2048 workgroups x 256 threads, nothing but v_exp_f32 in the loop."""
+    import torch
+    from masked_attention_forward_amd import binding as fb
+
+    out = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        n = fb.fa_exp2_rate_probe(out, iters)
+    torch.cuda.synchronize()
+    # Every thread's chains converge to 8 times the root of x = 2^(-x).
+    assert abs(float(out.min()) - 5.1294860) < 1e-4 and abs(float(out.max()) - 5.1294860) < 1e-4
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        fb.fa_exp2_rate_probe(out, iters)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return n * launches / (e0.elapsed_time(e1) * 1e-3)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(w, heads: int, decode: bool = False):
@@ -171,7 +213,7 @@ def cpu_baseline(w, heads: int, decode: bool = False):
         value, unit = moved / t_total / 1e9, "GB/s"
     else:
         value, unit = flops / t_total / 1e12, "TFLOP/s"
-    return {"value": value, "unit": unit, "cores": int(threads),
+    return {"value": value, "unit": unit, "cores": int(threads), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{len(sel)} of {w.B * w.N} (batch, head) slices at full Sq={w.Sq}, Skv={w.Skv}; "
                       f"{t_total:.1f} s of fp64 numpy (BLAS threads={threads}, elementwise on 1 core)"}
@@ -240,7 +282,7 @@ def bench_bwd(args, dev):
     def step():
         fb.fa_bwd(q, k, v, out, lse, do, dq, dk, dv, workspace=ws if ws_bytes else None, **kw)
 
-    pairs = visible_pairs(w, dev)
+    pairs, _ = visible_pairs(w, dev)
     flops = 10 * w.D * pairs
     n_pre = prewarm(step, args.prewarm_ms)
     for _ in range(args.warmup):
@@ -295,12 +337,27 @@ def bench_scatter(args, dev):
     ms = e0.elapsed_time(e1) / args.steps
     moved = 2 * 2 * T * N * D * 2 + T * 8   # K and V read + written, plus the slots
     gbs = moved / (ms * 1e-3) / 1e9
+    # Context: a plain device-to-device copy of the same K and V bytes (torch's copy kernel)
+    # on the same GPU, right after.
+    src = torch.cat([key.view(-1), val.view(-1)])
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * src.element_size() / (e0.elapsed_time(e1) / args.steps * 1e-3) / 1e9
+    del src, dst
     print(json.dumps({
         "metric": "paged KV cache scatter bandwidth (bytes read + written)", "value": round(gbs, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) keys/values, random distinct slots)",
         "timing": {"cache": "warm", "prewarm_ms": args.prewarm_ms, "prewarm_steps": n_pre},
+        "device_copy_gbs": round(copy_gbs, 1),
         "config": {"workload": "kv_scatter_prefill", "num_tokens": T, "N": N, "D": D, "num_blocks": nb,
                    "block_size": bs, "layout": "Norm"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -396,7 +453,7 @@ def main():
     else:
         def step():
             fb.fa_fwd(q, k, v, out, lse, **kw)
-    pairs = visible_pairs(w, dev)
+    pairs, computed_pairs = visible_pairs(w, dev)
     flops = 4 * w.D * pairs
     elem = q.element_size()
     rows_q = q.numel() // w.D
@@ -430,14 +487,18 @@ def main():
         timing = {"cache": "cold (512 MiB read before each launch; launches timed one by one)",
                   "ms_median": round(per[len(per) // 2], 4), "ms_min": round(per[0], 4)}
     else:
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
+        # One event between consecutive launches on the launching stream: the first-to-last span
+        # is the K-step timed region, and each gap is one launch (back to back, warm caches).
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i in range(args.steps):
             step()
-        e1.record(stream)
+            evs[i + 1].record(stream)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
+        ms = evs[0].elapsed_time(evs[-1]) / args.steps
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+        timing.update(ms_median=round(per[len(per) // 2], 4), ms_min=round(per[0], 4),
+                      ms_max=round(per[-1], 4))
     timing.update(prewarm_ms=args.prewarm_ms, prewarm_steps=n_pre)
     tflops = flops / (ms * 1e-3) / 1e12
     # At most 16 query rows per sequence: the split-KV decode path, bound by HBM.
@@ -478,6 +539,16 @@ def main():
                            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                            "algorithmic_bytes": alg_bytes, "kernel_sources_sha256": kernel_sources_sha()}
         res["config"]["effective_tflops"] = round(tflops, 3)
+    if not decode:
+        # Second roofline: one exp2 per computed score against the measured exp2 rate.
+        peak_exp = exp2_rate(dev)
+        achieved = computed_pairs / (ms * 1e-3)
+        res["exp_roofline"] = {"bound": "exp2 (v_exp_f32)", "achieved": round(achieved / 1e12, 3),
+                               "peak": round(peak_exp / 1e12, 3), "unit": "Texp/s",
+                               "frac": round(achieved / peak_exp, 4), "computed_pairs": computed_pairs,
+                               "visible_pairs": pairs,
+                               "visible_frac": round(pairs / (ms * 1e-3) / peak_exp, 4),
+                               "peak_source": "fa_exp2_rate_probe, 2048 x 256 threads, 64 x 128 exp2 each"}
     if not args.no_cpu_baseline and w.layout == "BNSD":
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads, decode)
     print(json.dumps(res), flush=True)

@@ -331,6 +331,23 @@ fa_status fa_fwd_paged(const void* q, const void* key_cache, const void* value_c
                        const fa_paged_kv* paged, float scale, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Measurement helper: the chip's base-2 exponential throughput.
+ * --------------------------------------------------------------------------------------- */
+
+/* The online softmax of the tiling page's recurrence evaluates one exponential per computed
+ * score, issued as the hardware exp2 instruction; its rate is the second roofline of the
+ * forward beside the matrix cores. This call launches `blocks` workgroups of 256 threads that
+ * issue nothing in their inner loop but that instruction, each thread iters * 128 times
+ * across 8 independent chains x <- 2^(-x).
+ *   out:             device float [blocks * 256]; thread t writes the sum of its 8 chains,
+ *                    which converge to 8 times the root of x = 2^(-x) (about 5.1295).
+ *   exps_per_launch: host, receives blocks * 256 * iters * 128.
+ * Errors: NULLPTR for a missing pointer, PARAM_INVALID for blocks or iters outside
+ * [1, 2^20], HIP for a launch error. Asynchronous on `stream`; time it with events there. */
+fa_status fa_exp2_rate_probe(float* out, int32_t blocks, int32_t iters, int64_t* exps_per_launch,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -108,6 +108,8 @@ def load_library():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, pdims, i32, i32, i64, i64, pi64, pi64, pi64,
                            vp, i32, vp, pi64, ctypes.c_float, vp, sz, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_exp2_rate_probe.argtypes = [vp, i32, i32, pi64, vp]
+    lib.fa_exp2_rate_probe.restype = i32
     _LIB = lib
     return lib
 
@@ -343,6 +345,20 @@ def fa_scatter_kv_cache(key, key_cache, slot_mapping, value=None, value_cache=No
                                  stream if stream is not None else _stream(key.device))
     if st != 0:
         raise FaError(st, "fa_scatter_kv_cache")
+
+
+def fa_exp2_rate_probe(out: torch.Tensor, iters: int, *, stream=None) -> int:
+    """Launch the exp2-throughput kernel over out.numel() // 256 workgroups (out: float32 on the
+    GPU); returns the number of exponentials the launch evaluates."""
+    _check_device_tensor("out", out, torch.float32)
+    if out.numel() == 0 or out.numel() % 256:
+        raise ValueError("out must hold a positive multiple of 256 floats")
+    n = ctypes.c_int64(0)
+    st = load_library().fa_exp2_rate_probe(_ptr(out), out.numel() // 256, int(iters), ctypes.byref(n),
+                                           stream if stream is not None else _stream(out.device))
+    if st != 0:
+        raise FaError(st, "fa_exp2_rate_probe")
+    return n.value
 
 
 def paged_kv(block_table: Optional[torch.Tensor], key_cache: torch.Tensor, *, cache_layout="Norm",

@@ -89,8 +89,8 @@ namespace {
 
 // Work item of this workgroup. Workgroups are dispatched round-robin over the 8 XCDs, each
 // with its own L2. Table mode (varlen / prefix): heads are the fastest index, so the blocks
-// of one (batch, head) share an XCD when N is a multiple of 8, and items run heaviest first
-// (the planner sorted the table). Fixed-length mode with xcd_major: XCD x = blockIdx % 8
+// of one (batch, head) share an XCD when N is a multiple of 8, and items run in the order of
+// the planner's table (sequence-major for varlen, longest first for prefix). Fixed-length mode with xcd_major: XCD x = blockIdx % 8
 // works through the (batch, head) pairs congruent to x one pair at a time, heaviest q tile
 // first, so each XCD streams the K/V of about one pair through its L2 at a time.
 

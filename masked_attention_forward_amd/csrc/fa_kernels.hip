@@ -2148,3 +2148,43 @@ extern "C" fa_status fa_mask_probe(const fa_dims* dims, int32_t layout, int32_t 
     if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
     return FA_OK;
 }
+
+// ------------------------------------------------------------------------------------------
+// Exp-throughput calibration. The online softmax evaluates one base-2 exponential per computed
+// score (the tiling page's recurrence, with exp rewritten as exp2 of log2(e)-scaled scores);
+// on this chip that is v_exp_f32, a transcendental issued at a fraction of the plain VALU rate.
+// This kernel issues nothing else in its loop: every thread runs FA_EXP_CHAINS independent
+// chains x <- 2^(-x) (the negation is a free source modifier), which converge to the root of
+// x = 2^(-x), so the values stay finite and the result can be checked.
+// ------------------------------------------------------------------------------------------
+
+constexpr int FA_EXP_CHAINS = 8;
+constexpr int FA_EXP_UNROLL = 16;
+constexpr int FA_EXP_THREADS = 256;
+
+__global__ __launch_bounds__(FA_EXP_THREADS) void fa_exp2_rate(float* out, int32_t iters) {
+    float x[FA_EXP_CHAINS];
+#pragma unroll
+    for (int c = 0; c < FA_EXP_CHAINS; ++c) x[c] = 0.5f + 0.0625f * float(c) + 0.001f * float(threadIdx.x & 7);
+    for (int32_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < FA_EXP_UNROLL; ++u) {
+#pragma unroll
+            for (int c = 0; c < FA_EXP_CHAINS; ++c) x[c] = __builtin_amdgcn_exp2f(-x[c]);
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < FA_EXP_CHAINS; ++c) s += x[c];
+    out[size_t(blockIdx.x) * FA_EXP_THREADS + threadIdx.x] = s;
+}
+
+extern "C" fa_status fa_exp2_rate_probe(float* out, int32_t blocks, int32_t iters, int64_t* exps_per_launch,
+                                        void* stream) {
+    if (!out || !exps_per_launch) return FA_ERR_NULLPTR;
+    if (blocks < 1 || iters < 1 || blocks > (1 << 20) || iters > (1 << 20)) return FA_ERR_PARAM_INVALID;
+    *exps_per_launch = int64_t(blocks) * FA_EXP_THREADS * iters * FA_EXP_UNROLL * FA_EXP_CHAINS;
+    (void)hipGetLastError();
+    fa_exp2_rate<<<dim3(unsigned(blocks)), dim3(FA_EXP_THREADS), 0, static_cast<hipStream_t>(stream)>>>(out, iters);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

@@ -460,10 +460,31 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
                     raw.push_back(int32_t(qt));
                 }
             }
-            // Longest first; ties keep batch-major order.
-            std::stable_sort(order.begin(), order.end(),
-                             [](const std::pair<int64_t, int64_t>& x,
-                                const std::pair<int64_t, int64_t>& y) { return x.first > y.first; });
+            // Varlen (TND) launches sequence-major: sequences by total cost, heaviest first, and
+            // in each its q tiles heaviest first. The workgroups an XCD runs at once then share
+            // one or two sequences' K/V in its L2 (longest-first over all sequences spreads them
+            // over many sequences and re-reads K/V from HBM about four times). Prefix modes on
+            // fixed-length batches launch longest first: their sequences are all long, and the
+            // balance of the global order matters more there. FA_TABLE_ORDER=seq|lpt forces.
+            const char* to = std::getenv("FA_TABLE_ORDER");
+            bool seq_major = tnd;
+            if (to && std::strcmp(to, "seq") == 0) seq_major = true;
+            if (to && std::strcmp(to, "lpt") == 0) seq_major = false;
+            if (seq_major) {
+                std::vector<int64_t> tot(B, 0);
+                for (const auto& o : order) tot[raw[2 * o.second]] += o.first;
+                std::stable_sort(order.begin(), order.end(),
+                                 [&](const std::pair<int64_t, int64_t>& x, const std::pair<int64_t, int64_t>& y) {
+                                     const int32_t bx = raw[2 * x.second], by = raw[2 * y.second];
+                                     if (bx != by) return tot[bx] != tot[by] ? tot[bx] > tot[by] : bx < by;
+                                     return x.first > y.first;
+                                 });
+            } else {
+                // Longest first; ties keep batch-major order.
+                std::stable_sort(order.begin(), order.end(),
+                                 [](const std::pair<int64_t, int64_t>& x,
+                                    const std::pair<int64_t, int64_t>& y) { return x.first > y.first; });
+            }
             p.items.resize(2 * order.size());
             for (size_t n = 0; n < order.size(); ++n) {
                 p.items[2 * n] = raw[2 * order[n].second];

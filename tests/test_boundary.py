@@ -41,6 +41,16 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_exp2_rate_probe_argument_checks(lib):
+    # Rejected before any device call, so these run without a GPU.
+    n = ctypes.c_int64(0)
+    assert lib.fa_exp2_rate_probe(None, 1, 1, ctypes.byref(n), None) == 1
+    fake = ctypes.c_void_p(256)
+    assert lib.fa_exp2_rate_probe(fake, 1, 1, None, None) == 1
+    for blocks, iters in ((0, 1), (1, 0), (-1, 5), (1 << 21, 1), (1, 1 << 21)):
+        assert lib.fa_exp2_rate_probe(fake, blocks, iters, ctypes.byref(n), None) == 2
+
+
 def test_status_strings(lib):
     for code in range(6):
         assert fb.fa_status_str(code).startswith(fb.STATUS_NAMES[code])

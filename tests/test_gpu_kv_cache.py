@@ -76,3 +76,21 @@ def test_scatter_prefill_size(gpu_device, layout):
     1024 x 16 cache written once."""
     _case(gpu_device, layout, torch.bfloat16, T=16384, N=32, dk=128, dv=128, nb=1024, bs=16,
           slot_dtype=torch.int64, seed=30)
+
+
+@pytest.mark.parametrize("grid", [None, "1", "3"])
+def test_scatter_segments_and_grid_stride(gpu_device, monkeypatch, grid):
+    """Work units of 256 chunks: token counts of 1 and odd sizes, rows that end inside a unit,
+    rows of several units (40 heads x D 128 = 1280 chunks), keys without values, padding slots;
+    with the grid capped at 1 and 3 workgroups each one walks many units (the path huge
+    inputs take)."""
+    if grid is not None:
+        monkeypatch.setenv("FA_SCATTER_GRID", grid)
+    for i, T in enumerate((1, 3, 5, 38)):
+        _case(gpu_device, "Norm", torch.bfloat16, T=T, N=3, dk=128, dv=64, nb=11, bs=16, slot_dtype=torch.int32,
+              seed=40 + i, bad_slots=min(2, T - 1))
+        _case(gpu_device, "NHSD", torch.float16, T=T, N=2, dk=24, dv=40, nb=7, bs=8, slot_dtype=torch.int64,
+              seed=50 + i, with_value=(i % 2 == 0))
+    _case(gpu_device, "Norm", torch.bfloat16, T=7, N=40, dk=128, dv=128, nb=4, bs=4, slot_dtype=torch.int64,
+          seed=60, bad_slots=1)
+    _case(gpu_device, "NHSD", torch.int8, T=6, N=5, dk=3, dv=7, nb=3, bs=4, slot_dtype=torch.int32, seed=61)
