@@ -526,13 +526,8 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
     auto load = [&](int kt, u32x4* dk, u32x4* dv) __attribute__((always_inline)) {
         bw_load2<D, BW2_THREADS>(kp, vp, kt * BW_T, kv_rs, kt < kr.end ? min(BW_T, g.skv - kt * BW_T) : 0, dk, dv);
     };
-    auto step = [&](auto s_tag, int kt) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_tag)::value;
-        using s3 = std::integral_constant<int, (S + 3) & 3>;
-        load(kt + 3, kbuf(s3{}), vbuf(s3{}));
-        const u32x4* kt_ = kbuf(s_tag);
-        const u32x4* vt_ = vbuf(s_tag);
-        f32x4 s[4], dp[4];
+    // S and dP of this wave's 16 rows against the 64 keys of a staged tile.
+    auto scores = [&](const u32x4* kt_, const u32x4* vt_, f32x4 (&s)[4], f32x4 (&dp)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
             s[bb] = f32x4{};
@@ -543,22 +538,30 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
                 dp[bb] = mm::mma(bw_arow<D>(vt_, lo, bb, kd), dop_[kd], dp[bb]);
             }
         }
+    };
+    // The scores of tile kt + 1 are computed one step ahead: their MFMAs are issued in between
+    // the elementwise work of tile kt, which does not depend on them, so the matrix cores run
+    // while this wave computes P and dS. Tiles where all of this wave's entries are visible
+    // (most of them) take a branch-free path with no per-entry mask test.
+    f32x4 sc[4], dpc[4];
+    auto ahead = [&](auto full_tag, auto s1_tag, int kt, u32x4 (&dsop)[2]) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        f32x4 sn[4], dpn[4];
+        scores(kbuf(s1_tag), vbuf(s1_tag), sn, dpn);   // tile kt + 1 (past the range: zeros, unused)
         const int j0 = kt * BW_T;
-        // Every (row, key) of this wave's 16 rows x 64 keys visible: no per-element test.
-        const bool full = fa_tile_full(g, wrow0, min(wrow0 + 15, g.sq - 1), j0, BW_T) && wrow0 + 15 < g.sq;
         float ds[16];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = j0 + 32 * (bb >> 1) + 8 * gq + 4 * (bb & 1) + e;
-                const bool vis = full || (row_ok && j >= row_lo && j <= row_hi);
-                const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[bb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - lse2)
-                                    : 0.f;
-                ds[4 * bb + e] = p * (dp[bb][e] - dlt);
+                const float x = AL ? fmaf(sc[bb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - lse2
+                                   : fmaf(sc[bb][e], sl2, -lse2);
+                float p = __builtin_amdgcn_exp2f(x);
+                if (!FULL) p = (row_ok & (j >= row_lo) & (j <= row_hi)) ? p : 0.f;
+                ds[4 * bb + e] = p * (dpc[bb][e] - dlt);
             }
         }
-        u32x4 dsop[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const float* lo = ds + 8 * kk;
@@ -566,11 +569,40 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
             dsop[kk] = u32x4{io::pack(lo[0], lo[1]), io::pack(lo[2], lo[3]), io::pack(hi[0], hi[1]),
                              io::pack(hi[2], hi[3])};
         }
+        if (FULL) {
+            // The next tile's 32 MFMAs, each with a share of the VALU work; their A operands
+            // are read from LDS six MFMAs ahead.
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // DS read
+#pragma unroll
+            for (int m = 0; m < 32; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                if (m < 26) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+            }
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            sc[bb] = sn[bb];
+            dpc[bb] = dpn[bb];
+        }
+    };
+    auto step = [&](auto s_tag, int kt) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_tag)::value;
+        using s1 = std::integral_constant<int, (S + 1) & 3>;
+        using s3 = std::integral_constant<int, (S + 3) & 3>;
+        load(kt + 3, kbuf(s3{}), vbuf(s3{}));
+        const u32x4* kt_ = kbuf(s_tag);
+        const int j0 = kt * BW_T;
+        // Every (row, key) of this wave's 16 rows x 64 keys visible: no per-entry test.
+        const bool full = fa_tile_full(g, wrow0, min(wrow0 + 15, g.sq - 1), j0, BW_T) && wrow0 + 15 < g.sq;
+        u32x4 dsop[2];
+        if (full) ahead(std::true_type{}, s1{}, kt, dsop);
+        else ahead(std::false_type{}, s1{}, kt, dsop);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) acc[db] = mm::mma(dsop[kk], bw_bcol<D>(kt_, lo, kk, db), acc[db]);
-        __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * LPT));   // tile kt + 1 has landed
+        __builtin_amdgcn_s_waitcnt(fa_vmcnt64(LPT));   // tile kt + 2 has landed
         bw_lds_barrier();
     };
     if (kr.begin < kr.end) {
@@ -581,8 +613,9 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
         load(kr.begin, k0, v0);
         load(kr.begin + 1, k1, v1);
         load(kr.begin + 2, k2, v2);
-        __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * LPT));   // Q, dO and tile 0
+        __builtin_amdgcn_s_waitcnt(fa_vmcnt64(LPT));   // Q, dO and tiles 0 and 1
         bw_lds_barrier();
+        scores(k0, v0, sc, dpc);
         // Trips of four; every path into a step runs the earlier ones.
         for (int kt = kr.begin; kt < kr.end; kt += 4) {
             step(c0{}, kt);
@@ -686,6 +719,11 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
     int r_lo, r_hi;
     bw_row_range(g, j0, min(j0 + BW2_BLOCK, g.skv) - 1, r_lo, r_hi);
     const int t_begin = r_lo / BW_T, t_end = r_lo <= r_hi ? r_hi / BW_T + 1 : t_begin;
+    // The rows that see this lane's key form one interval (both ends of a row's visible range
+    // grow with the row); for a single key bw_row_range is exact. None past the sequence's keys.
+    int key_row_lo, key_row_hi;
+    bw_row_range(g, j, j, key_row_lo, key_row_hi);
+    if (j >= g.skv) key_row_hi = -1;
 
     f32x4 dk[DB], dv[DB];
 #pragma unroll
@@ -749,10 +787,10 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = i0 + r0 + e;
-                    const bool vis = full || (i < g.sq && j < g.skv && j >= fa_row_lo(g, i) && j <= fa_row_hi(g, i));
-                    const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) -
-                                                                  l4[e] * kLog2e)
-                                         : 0.f;
+                    const float x = AL ? fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - l4[e] * kLog2e
+                                       : fmaf(s[rb][e], sl2, -l4[e] * kLog2e);
+                    const bool vis = full || (i >= key_row_lo && i <= key_row_hi);
+                    const float pv = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
                     p[4 * r2 + e] = pv;
                     ds[4 * r2 + e] = pv * (dp[rb][e] - d4[e]);
                 }
