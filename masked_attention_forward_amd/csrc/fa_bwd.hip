@@ -465,6 +465,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
     constexpr int LPT = 2 * TILE_U4 / BW2_THREADS;   // direct loads per thread and kv tile (K and V)
     __shared__ u32x4 k0[TILE_U4], k1[TILE_U4], k2[TILE_U4], k3[TILE_U4];
     __shared__ u32x4 v0[TILE_U4], v1[TILE_U4], v2[TILE_U4], v3[TILE_U4];
+    FA_POISON_LDS(k0, k1, k2, k3, v0, v1, v2, v3);
     auto kbuf = [&](auto s_tag) __attribute__((always_inline)) -> u32x4* {
         constexpr int S = decltype(s_tag)::value & 3;
         if constexpr (S == 0) return k0;
@@ -653,6 +654,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
     __shared__ u32x4 o0[TILE_U4], o1[TILE_U4], o2[TILE_U4], o3[TILE_U4];
     __shared__ __attribute__((aligned(16))) float l0[BW_T], l1[BW_T], l2[BW_T], l3[BW_T];
     __shared__ __attribute__((aligned(16))) float d0[BW_T], d1[BW_T], d2[BW_T], d3[BW_T];
+    FA_POISON_LDS(q0, q1, q2, q3, o0, o1, o2, o3, l0, l1, l2, l3, d0, d1, d2, d3);
     auto qbuf = [&](auto s_tag) __attribute__((always_inline)) -> u32x4* {
         constexpr int S = decltype(s_tag)::value & 3;
         if constexpr (S == 0) return q0;

@@ -21,6 +21,31 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// Debug builds (FA_LDS_POISON defined) fill a kernel's LDS tiles with all-ones words before its
+// first load: 0xFFFF is a NaN in bf16 and fp16 and 0xFFFFFFFF one in fp32, so a read of any
+// byte that no load or store of the kernel wrote (a tile row past a sequence that was not
+// zero-filled, say) turns outputs into NaN, even where the value is multiplied by a zero
+// probability. The library built this way is a separate file; the tests compare its outputs
+// with the normal library's bit for bit. Without the flag FA_POISON_LDS expands to nothing.
+#ifdef FA_LDS_POISON
+template <typename T, int N>
+__device__ __forceinline__ void fa_poison_one(T (&a)[N]) {
+    static_assert(sizeof(a) % 4 == 0, "LDS arrays are whole words");
+    uint32_t* w = reinterpret_cast<uint32_t*>(a);
+    for (int i = int(threadIdx.x); i < int(sizeof(a) / 4); i += int(blockDim.x)) w[i] = 0xFFFFFFFFu;
+}
+template <typename... A>
+__device__ __forceinline__ void fa_poison_lds(A&... a) {
+    (fa_poison_one(a), ...);
+    __syncthreads();
+}
+#define FA_POISON_LDS(...) fa_poison_lds(__VA_ARGS__)
+#else
+#define FA_POISON_LDS(...) \
+    do {                   \
+    } while (0)
+#endif
+
 // Values read from the workspace tables are the same for every lane; readfirstlane keeps them
 // in scalar registers (buffer descriptors built from them must be wave-uniform).
 __device__ __forceinline__ int fa_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

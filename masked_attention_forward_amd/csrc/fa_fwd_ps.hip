@@ -72,6 +72,7 @@ fa_fwd_ps(const fa_kargs a, const fa_ps_args ps) {
     // O staging: a 32-row slot per wave of a group. The two groups write out items in different
     // phases (B one phase behind A, a barrier between), so waves w and w + 4 share slot w % 4.
     __shared__ u32x4 lds_o[4 * 32 * KCH];
+    FA_POISON_LDS(lds_k0, lds_k1, lds_k2, lds_k3, lds_v0, lds_v1, lds_v2, lds_v3, lds_o);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;

@@ -87,6 +87,7 @@ fa_fwd_mfma(const fa_kargs a) {
     // wait for it before those reads.
     __shared__ u32x4 lds_k0[TILE_CHUNKS], lds_k1[TILE_CHUNKS];
     __shared__ u32x4 lds_v0[TILE_CHUNKS], lds_v1[TILE_CHUNKS];
+    FA_POISON_LDS(lds_k0, lds_k1, lds_v0, lds_v1);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -423,6 +424,7 @@ fa_fwd_pp(const fa_kargs a) {
 
     __shared__ u32x4 lds_k0[TILE_CHUNKS], lds_k1[TILE_CHUNKS], lds_k2[TILE_CHUNKS], lds_k3[TILE_CHUNKS];
     __shared__ u32x4 lds_v0[TILE_CHUNKS], lds_v1[TILE_CHUNKS], lds_v2[TILE_CHUNKS], lds_v3[TILE_CHUNKS];
+    FA_POISON_LDS(lds_k0, lds_k1, lds_k2, lds_k3, lds_v0, lds_v1, lds_v2, lds_v3);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -962,6 +964,7 @@ __global__ __launch_bounds__(DC_THREADS) void fa_decode_split(const fa_kargs a, 
     constexpr int DB = D / 16;                 // 16-column blocks of O
     constexpr int TILE_U4 = DC_BN * D / 8;     // 16-byte chunks of a tile
     __shared__ u32x4 lds_v[4 * 2 * TILE_U4];   // per wave, two V tiles
+    FA_POISON_LDS(lds_v);
 
     const int lane = threadIdx.x & 63;
     const int wave = fa_uniform(threadIdx.x >> 6);
