@@ -176,7 +176,8 @@ fa_status fa_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
  *   dout:             device, dims->dtype, out's layout.
  *   dq, dk, dv:       device, dims->dtype, the layouts of q, k and v; every element is written
  *                     (zero where no visible pair contributes).
- *   workspace:        at least fa_bwd_workspace_size bytes (Delta, and the per-batch geometry in
+ *   workspace:        at least fa_bwd_workspace_size bytes (Delta and the LSE scaled to log2
+ *                     units, each laid out like softmax_lse, and the per-batch geometry in
  *                     TND / prefix modes).
  * Every other argument, its validation and the status codes are fa_fwd's. Gradients accumulate
  * in fp32; with fp16 / bf16 inputs P and dS are rounded to that type for the products that

@@ -44,6 +44,7 @@ struct fa_bwd_args {
     void* dv;
     const float* lse;
     float* delta;            // laid out like lse (workspace)
+    float* lse2;             // lse * log2(e), laid out like lse (workspace)
     const float* slopes;
     const uint8_t* mask;
     const fa_geom* geoms;    // per-batch table (workspace) or nullptr
@@ -140,7 +141,11 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_delta(const fa_bwd_args a) 
     for (int d = lane; d < a.D; d += 64) s = fmaf(to_f(op[d]), to_f(dp[d]), s);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-    if (lane == 0) a.delta[b * a.lse_bs + h * a.lse_hs + g.q_start + i] = s;
+    if (lane == 0) {
+        const int64_t li = b * a.lse_bs + h * a.lse_hs + g.q_start + i;
+        a.delta[li] = s;
+        a.lse2[li] = a.lse[li] * kLog2e;
+    }
 }
 
 // bf16 / fp16 with D % 8 == 0 and 16-byte aligned rows: 16 lanes per row, 16 bytes per lane and
@@ -179,7 +184,11 @@ __global__ __launch_bounds__(BW_THREADS) void fa_bwd_delta_v(const fa_bwd_args a
     // Every lane takes part in the reduction over its 16-lane row group.
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-    if (c == 0 && i < g.sq) a.delta[b * a.lse_bs + h * a.lse_hs + g.q_start + i] = s;
+    if (c == 0 && i < g.sq) {
+        const int64_t li = b * a.lse_bs + h * a.lse_hs + g.q_start + i;
+        a.delta[li] = s;
+        a.lse2[li] = a.lse[li] * kLog2e;
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -698,7 +707,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
     const int64_t ko = b * a.kv_bs + h * a.kv_hs + int64_t(g.kv_start) * a.kv_rs;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qo;
     const uint16_t* dop = static_cast<const uint16_t*>(a.dout) + qo;
-    const float* lsep = a.lse + b * a.lse_bs + h * a.lse_hs + g.q_start;
+    const float* lsep = a.lse2 + b * a.lse_bs + h * a.lse_hs + g.q_start;
     const float* dlp = a.delta + b * a.lse_bs + h * a.lse_hs + g.q_start;
 
     // This lane's key (the S column) and its operands.
@@ -733,8 +742,9 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
         dk[db] = f32x4{};
         dv[db] = f32x4{};
     }
-    // q tile t (none past the range: zeros, nothing read): Q and dO by every wave; LSE and
-    // Delta (natural log and plain; rows past the sequence read as zeros) by wave 0.
+    // q tile t (none past the range: zeros, nothing read): Q and dO by every wave; the LSE in
+    // log2 units (as the Delta kernel wrote it) and Delta (rows past the sequence read as zeros)
+    // by wave 0.
     auto load = [&](int t, u32x4* dq_, u32x4* ddo, float* dl, float* ddl) __attribute__((always_inline)) {
         const int rows = t < t_end ? min(BW_T, g.sq - t * BW_T) : 0;
         bw_load2<D, BW2_THREADS>(qp, dop, t * BW_T, q_rs, rows, dq_, ddo);
@@ -778,7 +788,9 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
             }
         };
         // P and dS of the half's 32 rows x this lane's key, packed as the dV / dK left operands.
-        auto soft = [&](int hf) __attribute__((always_inline)) {
+        // FULL (every entry of the tile visible for this wave, most tiles): no mask test at all.
+        auto soft = [&](auto full_tag, int hf) __attribute__((always_inline)) {
+            constexpr bool FULL = decltype(full_tag)::value;
             float p[8], ds[8];
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2) {
@@ -789,10 +801,10 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = i0 + r0 + e;
-                    const float x = AL ? fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - l4[e] * kLog2e
-                                       : fmaf(s[rb][e], sl2, -l4[e] * kLog2e);
-                    const bool vis = full || (i >= key_row_lo && i <= key_row_hi);
-                    const float pv = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
+                    const float x = AL ? fmaf(s[rb][e], sl2, bw_bias2<AL>(slope2, i, j, off, aoff)) - l4[e]
+                                       : fmaf(s[rb][e], sl2, -l4[e]);
+                    float pv = __builtin_amdgcn_exp2f(x);
+                    if (!FULL) pv = (i >= key_row_lo && i <= key_row_hi) ? pv : 0.f;
                     p[4 * r2 + e] = pv;
                     ds[4 * r2 + e] = pv * (dp[rb][e] - d4[e]);
                 }
@@ -808,10 +820,12 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
             }
         };
         sdp(0);
-        soft(0);
+        if (full) soft(std::true_type{}, 0);
+        else soft(std::false_type{}, 0);
         sdp(1);
         dvdk(0);
-        soft(1);
+        if (full) soft(std::true_type{}, 1);
+        else soft(std::false_type{}, 1);
         dvdk(1);
         // q tile t + 1 has landed (wave 0 issues two more loads per tile).
         if (wave == 0) __builtin_amdgcn_s_waitcnt(fa_vmcnt64(2 * (LPT + 2)));
@@ -865,7 +879,7 @@ struct bw_plan {
     fa_plan p;
     bool mfma = false;
     int32_t n_qt = 0, n_kt = 0;
-    size_t ws_delta_offset = 0, ws_bytes = 0;
+    size_t ws_delta_offset = 0, ws_lse2_offset = 0, ws_bytes = 0;
     int64_t lse_elems = 0;
 };
 
@@ -897,6 +911,8 @@ fa_status make_bw_plan(const fa_call& c, bool sizes_only, bw_plan* out) {
     size_t off = 0;
     if (p.table) off = (size_t(d.B) * sizeof(fa_geom) + 255) & ~size_t(255);
     bp.ws_delta_offset = off;
+    off = (off + size_t(bp.lse_elems) * sizeof(float) + 255) & ~size_t(255);
+    bp.ws_lse2_offset = off;
     off += size_t(bp.lse_elems) * sizeof(float);
     bp.ws_bytes = (p.rows_total == 0 && p.kv_total == 0) ? 0 : ((off + 255) & ~size_t(255));
     *out = std::move(bp);
@@ -1027,6 +1043,7 @@ extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const v
     a.dv = dv;
     a.lse = softmax_lse;
     a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + bp.ws_delta_offset);
+    a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bp.ws_lse2_offset);
     a.slopes = alibi_slopes;
     a.mask = atten_mask;
     a.geoms = p.table ? static_cast<const fa_geom*>(workspace) : nullptr;
