@@ -487,12 +487,13 @@ def test_bwd_validation_and_workspace(lib):
     assert call(alibi_mode=5) == INVALID
     assert call(dims=bnsd(D=129)) == UNSUPPORTED
     need = fb.fa_bwd_workspace_size(d, "BNSD", 3)
-    assert need == _align256(2 * 4 * 64 * 4)
+    # Delta and the log2-scaled LSE, each laid out like softmax_lse and 256-byte aligned.
+    assert need == 2 * _align256(2 * 4 * 64 * 4)
     assert call(wsb=need - 1) == WORKSPACE
     assert call(ws=None, wsb=0) == NULLPTR
     dt = tnd([3, 0, 9], [5, 7, 0])
     need_t = fb.fa_bwd_workspace_size(dt, "TND", 3, [3, 3, 12], [5, 12, 12])
-    assert need_t == _align256(3 * 32) + _align256(2 * 12 * 4)
+    assert need_t == _align256(3 * 32) + 2 * _align256(2 * 12 * 4)
     # nothing at all to do: OK without pointers
     d0 = bnsd(B=0)
     assert lib.fa_bwd(None, None, None, None, None, None, None, None, None, ctypes.byref(d0), 0, 3, 0, 0, None, None,
