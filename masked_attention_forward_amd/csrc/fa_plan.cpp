@@ -531,7 +531,22 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
                 }
                 return end;
             };
-            bool rank = ppx > 1 && nq > 1 && makespan(true) * 20 < makespan(false) * 19;
+            // Workgroups are dispatched in launch order, so a workgroup that cannot start yet holds
+            // back the ones after it: in pair-major order, where neighbouring items differ a lot in
+            // cost (causal: the heaviest q tile of a pair next to its lightest), compute units
+            // measured idle for 4-32 us between items. When the item costs of a pair spread
+            // widely (coefficient of variation above 0.35; band masks stay near 0.2), take the
+            // rank-major order, whose neighbours cost the same.
+            double cs = 0.0, cs2 = 0.0;
+            for (int32_t r = 0; r < nq; ++r) {
+                cs += double(cost[r]);
+                cs2 += double(cost[r]) * double(cost[r]);
+            }
+            const double mean = cs / std::max(nq, 1), var = std::max(cs2 / std::max(nq, 1) - mean * mean, 0.0);
+            // Mode 1's costs come from the mask on the device; its pre-pass launches each slice's
+            // q tiles most visited first, so pair-major neighbours differ as much as causal ones.
+            const bool spread = nq > 1 && (p.dense_tiles || std::sqrt(var) > 0.35 * mean);
+            bool rank = ppx > 1 && nq > 1 && (spread || makespan(true) * 20 < makespan(false) * 19);
             const char* xo = std::getenv("FA_XCD_ORDER");
             if (xo && std::strcmp(xo, "rank") == 0) rank = true;
             if (xo && std::strcmp(xo, "pair") == 0) rank = false;
