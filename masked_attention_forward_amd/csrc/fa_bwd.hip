@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "fa_device.h"
@@ -56,6 +58,7 @@ struct fa_bwd_args {
     int32_t B, N, D;
     int32_t n_qt, n_kt;      // 64-row q tiles / 64-key kv tiles of the longest sequence
     int32_t alibi_left;
+    int32_t rank_order;      // MFMA kernels: non-zero = rank-major block order (bw_block)
     float scale_log2;        // scale * log2(e)
     float scale;
 };
@@ -92,11 +95,18 @@ __device__ __forceinline__ void bw_row_range(const fa_geom& g, int j0, int j1, i
 // so every XCD gets the same mix of light and heavy blocks (block b otherwise lands on XCD
 // b % 8 for every pair, and under causal masks the work grows with b) and a pair's K / V stay in
 // one L2. reverse: hand out the blocks last first (dQ, whose last blocks see the most keys).
-__device__ __forceinline__ void bw_block(int w, int pairs, int nblk, bool reverse, int& pair, int& blk) {
+__device__ __forceinline__ void bw_block(int w, int pairs, int nblk, bool reverse, bool rank, int& pair, int& blk) {
     if ((pairs & 7) == 0) {
         const int x = w & 7, s = w >> 3;
-        pair = (s / nblk) * 8 + x;
-        blk = s % nblk;
+        if (rank) {
+            // Rank-major: block r of every pair of the XCD, then block r + 1.
+            const int ppx = pairs >> 3;
+            pair = (s % ppx) * 8 + x;
+            blk = s / ppx;
+        } else {
+            pair = (s / nblk) * 8 + x;
+            blk = s % nblk;
+        }
     } else {
         pair = w / nblk;
         blk = w % nblk;
@@ -494,7 +504,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
     const bw_offsets<D> lo(n, gq);
     const int nqb = (a.n_qt * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
     int bh, qb;
-    bw_block(blockIdx.x, a.B * a.N, nqb, true, bh, qb);
+    bw_block(blockIdx.x, a.B * a.N, nqb, true, a.rank_order != 0, bh, qb);
     const int b = bh / a.N, h = bh % a.N;
     const fa_geom g = bw_geom(a, b);
     const int i0 = qb * BW2_BLOCK;
@@ -697,7 +707,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
     const bw_offsets<D> lo(n, gq);
     const int nkb = (a.n_kt * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
     int bh, kb;
-    bw_block(blockIdx.x, a.B * a.N, nkb, false, bh, kb);
+    bw_block(blockIdx.x, a.B * a.N, nkb, false, a.rank_order != 0, bh, kb);
     const int b = bh / a.N, h = bh % a.N;
     const fa_geom g = bw_geom(a, b);
     const int j0 = kb * BW2_BLOCK;
@@ -952,8 +962,17 @@ template <int D, bool BF, int AL>
 void launch_mfma(const fa_bwd_args& a, int64_t pairs, hipStream_t s) {
     const int64_t nqb = (int64_t(a.n_qt) * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
     const int64_t nkb = (int64_t(a.n_kt) * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
-    if (nkb > 0) fa_bwd_dkdv_mfma<D, BF, AL><<<dim3(unsigned(pairs * nkb)), dim3(BW2_THREADS), 0, s>>>(a);
-    if (nqb > 0) fa_bwd_dq_mfma<D, BF, AL><<<dim3(unsigned(pairs * nqb)), dim3(BW2_THREADS), 0, s>>>(a);
+    // Block order: host code 1 = the forward planner took rank-major (item costs spread widely),
+    // 2 / 3 = forced rank / pair. Rank-major pays off only while a pair has few blocks: with
+    // many, neighbouring blocks of a pair differ little in cost. Same box, rank-major against
+    // pair-major: causal_2048 (16 blocks a pair) +9%, causal_8192 (64) -0.5%.
+    auto order = [&](int64_t nblk) {
+        fa_bwd_args c = a;
+        c.rank_order = a.rank_order == 2 || (a.rank_order == 1 && nblk <= 32) ? 1 : 0;
+        return c;
+    };
+    if (nkb > 0) fa_bwd_dkdv_mfma<D, BF, AL><<<dim3(unsigned(pairs * nkb)), dim3(BW2_THREADS), 0, s>>>(order(nkb));
+    if (nqb > 0) fa_bwd_dq_mfma<D, BF, AL><<<dim3(unsigned(pairs * nqb)), dim3(BW2_THREADS), 0, s>>>(order(nqb));
 }
 
 template <int D, bool BF>
@@ -1058,6 +1077,11 @@ extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const v
     a.n_qt = bp.n_qt;
     a.n_kt = bp.n_kt;
     a.alibi_left = alibi_mode == FA_ALIBI_LEFT ? 1 : 0;
+    {
+        // FA_BWD_ORDER=rank|pair forces the MFMA kernels' block order (comparisons).
+        const char* e = std::getenv("FA_BWD_ORDER");
+        a.rank_order = e && std::strcmp(e, "rank") == 0 ? 2 : (e && std::strcmp(e, "pair") == 0 ? 3 : (p.xcd_major == 2 ? 1 : 0));
+    }
     a.scale_log2 = scale * kLog2e;
     a.scale = scale;
     const int al = alibi_slopes == nullptr ? 0 : (alibi_mode == FA_ALIBI_SQRT ? 2 : 1);
