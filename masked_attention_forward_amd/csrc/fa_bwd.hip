@@ -1080,7 +1080,7 @@ extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const v
     {
         // FA_BWD_ORDER=rank|pair forces the MFMA kernels' block order (comparisons).
         const char* e = std::getenv("FA_BWD_ORDER");
-        a.rank_order = e && std::strcmp(e, "rank") == 0 ? 2 : (e && std::strcmp(e, "pair") == 0 ? 3 : (p.xcd_major == 2 ? 1 : 0));
+        a.rank_order = e && std::strcmp(e, "rank") == 0 ? 2 : (e && std::strcmp(e, "pair") == 0 ? 3 : (p.xcd_major >= 2 ? 1 : 0));
     }
     a.scale_log2 = scale * kLog2e;
     a.scale = scale;

@@ -120,10 +120,19 @@ __device__ __forceinline__ void fa_decode_item(const fa_kargs& a, int& b, int& h
     } else if (a.xcd_major) {
         // Pair-major (1): the pairs of XCD x one after another, each heaviest q tile first.
         // Rank-major (2): the heaviest q tile of every pair of XCD x, then the next rank.
+        // Grouped rank-major (3): rank-major over four pairs of XCD x at a time.
         const int x = w & 7, slot = w >> 3;
         const int ppx = a.B * a.N / 8;
-        const int pair = (a.xcd_major == 2 ? slot % ppx : slot / a.n_qtiles_fixed) * 8 + x;
-        const int r = a.xcd_major == 2 ? slot / ppx : slot % a.n_qtiles_fixed;
+        int pair, r;
+        if (a.xcd_major == 3) {
+            // Rank-major within groups of four pairs (the planner keeps (B N / 8) % 4 == 0).
+            const int nq = a.n_qtiles_fixed, gr = slot / (4 * nq), jj = slot % (4 * nq);
+            pair = (gr * 4 + (jj & 3)) * 8 + x;
+            r = jj >> 2;
+        } else {
+            pair = (a.xcd_major == 2 ? slot % ppx : slot / a.n_qtiles_fixed) * 8 + x;
+            r = a.xcd_major == 2 ? slot / ppx : slot % a.n_qtiles_fixed;
+        }
         b = pair / a.N;
         h = pair % a.N;
         qt = a.reverse_qt ? a.n_qtiles_fixed - 1 - r : r;
