@@ -58,7 +58,7 @@ struct fa_bwd_args {
     int32_t B, N, D;
     int32_t n_qt, n_kt;      // 64-row q tiles / 64-key kv tiles of the longest sequence
     int32_t alibi_left;
-    int32_t rank_order;      // MFMA kernels: non-zero = rank-major block order (bw_block)
+    int32_t rank_order;      // MFMA kernels: 1 = rank-major block order, 2 = in groups of four pairs (bw_block)
     float scale_log2;        // scale * log2(e)
     float scale;
 };
@@ -95,14 +95,22 @@ __device__ __forceinline__ void bw_row_range(const fa_geom& g, int j0, int j1, i
 // so every XCD gets the same mix of light and heavy blocks (block b otherwise lands on XCD
 // b % 8 for every pair, and under causal masks the work grows with b) and a pair's K / V stay in
 // one L2. reverse: hand out the blocks last first (dQ, whose last blocks see the most keys).
-__device__ __forceinline__ void bw_block(int w, int pairs, int nblk, bool reverse, bool rank, int& pair, int& blk) {
+__device__ __forceinline__ void bw_block(int w, int pairs, int nblk, bool reverse, bool rank, bool rank_grouped,
+                                         int& pair, int& blk) {
     if ((pairs & 7) == 0) {
         const int x = w & 7, s = w >> 3;
         if (rank) {
-            // Rank-major: block r of every pair of the XCD, then block r + 1.
+            // Rank-major: block r of every pair of the XCD, then block r + 1; in groups of four
+            // pairs when the XCD's pairs split that way (rank == 2), as the forward does.
             const int ppx = pairs >> 3;
-            pair = (s % ppx) * 8 + x;
-            blk = s / ppx;
+            if (rank_grouped && (ppx & 3) == 0 && ppx > 4) {
+                const int gr = s / (4 * nblk), jj = s % (4 * nblk);
+                pair = (gr * 4 + (jj & 3)) * 8 + x;
+                blk = jj >> 2;
+            } else {
+                pair = (s % ppx) * 8 + x;
+                blk = s / ppx;
+            }
         } else {
             pair = (s / nblk) * 8 + x;
             blk = s % nblk;
@@ -504,7 +512,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dq_mfma(const fa_bwd_args 
     const bw_offsets<D> lo(n, gq);
     const int nqb = (a.n_qt * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
     int bh, qb;
-    bw_block(blockIdx.x, a.B * a.N, nqb, true, a.rank_order != 0, bh, qb);
+    bw_block(blockIdx.x, a.B * a.N, nqb, true, a.rank_order != 0, a.rank_order == 2, bh, qb);
     const int b = bh / a.N, h = bh % a.N;
     const fa_geom g = bw_geom(a, b);
     const int i0 = qb * BW2_BLOCK;
@@ -707,7 +715,7 @@ __global__ __launch_bounds__(BW2_THREADS) void fa_bwd_dkdv_mfma(const fa_bwd_arg
     const bw_offsets<D> lo(n, gq);
     const int nkb = (a.n_kt * BW_T + BW2_BLOCK - 1) / BW2_BLOCK;
     int bh, kb;
-    bw_block(blockIdx.x, a.B * a.N, nkb, false, a.rank_order != 0, bh, kb);
+    bw_block(blockIdx.x, a.B * a.N, nkb, false, a.rank_order != 0, a.rank_order == 2, bh, kb);
     const int b = bh / a.N, h = bh % a.N;
     const fa_geom g = bw_geom(a, b);
     const int j0 = kb * BW2_BLOCK;
@@ -966,9 +974,11 @@ void launch_mfma(const fa_bwd_args& a, int64_t pairs, hipStream_t s) {
     // 2 / 3 = forced rank / pair. Rank-major pays off only while a pair has few blocks: with
     // many, neighbouring blocks of a pair differ little in cost. Same box, rank-major against
     // pair-major: causal_2048 (16 blocks a pair) +9%, causal_8192 (64) -0.5%.
+    const char* ge = std::getenv("FA_BWD_GROUPED");
+    const bool grouped = !(ge && ge[0] == '0');
     auto order = [&](int64_t nblk) {
         fa_bwd_args c = a;
-        c.rank_order = a.rank_order == 2 || (a.rank_order == 1 && nblk <= 32) ? 1 : 0;
+        c.rank_order = a.rank_order == 2 || (a.rank_order == 1 && nblk <= 32) ? (grouped ? 2 : 1) : 0;
         return c;
     };
     if (nkb > 0) fa_bwd_dkdv_mfma<D, BF, AL><<<dim3(unsigned(pairs * nkb)), dim3(BW2_THREADS), 0, s>>>(order(nkb));
