@@ -236,6 +236,11 @@ typedef struct fa_plan_stats {
     int64_t kv_tiles_full;     /* of which need no per-element masking                  */
     int64_t kv_tiles_total;    /* kv tiles a dense pass would load, per head            */
     size_t workspace_bytes;
+    int32_t launch_order;      /* prefill work-item order: 0 batch-major, 1 pair-major,
+                                  2 rank-major, 3 rank-major in groups of four pairs (the
+                                  last three XCD-major), 4 a work table (varlen / prefix);
+                                  0 for the split-KV decode kernel */
+    int32_t reserved;
 } fa_plan_stats;
 
 fa_status fa_plan_stats_get(const fa_dims* dims, int32_t layout, int32_t sparse_mode,

@@ -31,7 +31,8 @@ class FaPlanStats(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
                 ("work_items", ctypes.c_int64), ("kv_tiles_visited", ctypes.c_int64),
                 ("kv_tiles_full", ctypes.c_int64), ("kv_tiles_total", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("launch_order", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):

@@ -711,6 +711,8 @@ extern "C" fa_status fa_plan_stats_get(const fa_dims* dims, int32_t layout, int3
     out->kv_tiles_full = p.kv_tiles_full;
     out->kv_tiles_total = p.kv_tiles_total;
     out->workspace_bytes = p.ws_bytes;
+    out->launch_order = p.kernel == FA_KERNEL_DECODE ? 0 : (p.table ? 4 : p.xcd_major);
+    out->reserved = 0;
     return FA_OK;
 }
 

@@ -581,3 +581,24 @@ def test_noalloc_validates_and_refuses_oversize_before_device_work(lib):
     st = lib.fa_fwd_noalloc(None, p, p, p, p, ctypes.byref(bnsd()), 0, 3, 0, 0, None, None, None, None, 0, None,
                             None, 0.125, None)
     assert st == NULLPTR
+
+
+def test_launch_order_choice(lib):
+    """The planner's forward launch order (fa_plan_stats.launch_order): rank-major in groups of
+    four pairs where item costs spread widely (causal) or come from a mask (mode 1), pair-major
+    for bands, batch-major when the (batch, head) pairs do not split over the 8 XCDs, a table for
+    varlen and prefix modes, 0 for the decode kernel."""
+    def order(dims, layout, mode, **kw):
+        return fb.fa_plan_stats(dims, layout, mode, scale=0.088, **kw)["launch_order"]
+
+    big = fb.make_dims(2, 0, B=2, N=32, Sq=8192, Skv=8192, D=128)
+    assert order(big, "BNSD", 3) == 3
+    assert order(fb.make_dims(2, 0, B=4, N=32, Sq=2048, Skv=2048, D=128), "BNSD", 3) == 3
+    assert order(big, "BNSD", 4, pre_tokens=1024, next_tokens=0) == 1
+    assert order(big, "BNSD", 0, pre_tokens=1024, next_tokens=-256) == 1
+    assert order(big, "BNSD", 1, has_mask=True) == 3
+    assert order(fb.make_dims(2, 0, B=1, N=4, Sq=4096, Skv=4096, D=128), "BNSD", 3) == 0
+    assert order(big, "BNSD", 5, prefix=[100, 2000]) == 4
+    tq = fb.make_dims(2, 2, B=2, N=32, D=128, T_q=3000, T_kv=3000)
+    assert order(tq, "TND", 3, actual_seq_qlen=[1000, 3000], actual_seq_kvlen=[1000, 3000]) == 4
+    assert order(fb.make_dims(2, 0, B=4, N=32, Sq=1, Skv=32768, D=128), "BNSD", 3) == 0
