@@ -449,6 +449,12 @@ fa_fwd_pp(const fa_kargs a) {
     const fa_kv_range kr = fa_tile_kv_range(g, i0, i_last, BN);
     int n_tiles = kr.end - kr.begin;
     int kv_lim = min(kr.end * BN, g.skv);
+    // Kernels with an alibi bias walk the item's kv tiles from the last to the first: the bias
+    // rises with the key index, so the row maximum then shows up in the first tiles and the
+    // softmax's fast path (see there) holds for the rest. Positions t >= n_tiles map past the
+    // range on either side; their loads read nothing.
+    constexpr bool REV = ALIBI && !DENSE;
+    auto kt_of = [&](int t) __attribute__((always_inline)) { return REV ? kr.end - 1 - t : kr.begin + t; };
     // Dense mask: the kv tiles come from the pre-pass's list for this q tile (a count, then per
     // visited tile kt | full-wave bits << 24), and the per-element mask from its packed bits.
     // Entries are read by scalar loads through the constant address space (the tables do not
@@ -522,8 +528,8 @@ fa_fwd_pp(const fa_kargs a) {
     // Page id of key tile kt (-1 past the item's range: that load reads nothing).
     auto page_of = [&](int kt) __attribute__((always_inline)) {
         if constexpr (PAGED) {
-            const int pg = bt_row[min((kt * BN) >> lbs, pg_last)];
-            return kt < kr.end ? pg : -1;
+            const int pg = bt_row[max(min((kt * BN) >> lbs, pg_last), 0)];
+            return kt < kr.end && kt >= kr.begin ? pg : -1;
         } else {
             return 0;
         }
@@ -550,8 +556,8 @@ fa_fwd_pp(const fa_kargs a) {
     // Tile kt of K or V; `page` is its page id (paged K / V only). Rows past kv_lim, and every
     // row of a page id outside [0, num_pages), read as zeros.
     auto dload = [&](const uint16_t* base, int kt, int page, u32x4* dst) __attribute__((always_inline)) {
-        const int j0 = kt * BN;
-        int rows = min(BN, kv_lim - j0);
+        const int j0 = max(kt, 0) * BN;
+        int rows = REV && kt < kr.begin ? 0 : min(BN, kv_lim - j0);
         const uint16_t* tile = base + int64_t(j0) * kv_rs;
         if constexpr (PAGED) {
             // Page bytes and in-page offsets fit 32 bits (checked on the host): one 32 x 32 -> 64
@@ -604,7 +610,7 @@ fa_fwd_pp(const fa_kargs a) {
     // O^T rescale happens here too: no MFMA of this wave is using the accumulators.
     // es: the dense-mask entry of tile t; hidden: its packed mask bits for this lane.
     auto softmax = [&](int t, uint32_t es, uint32_t hidden) __attribute__((always_inline)) {
-        const int j0 = DENSE ? int(es & FA_DENSE_KT) * BN : (kr.begin + t) * BN;
+        const int j0 = DENSE ? int(es & FA_DENSE_KT) * BN : kt_of(t) * BN;
         const bool full = DENSE ? ((es >> (24 + wave_u)) & 1u) != 0u : fa_tile_full(g, wrow0, wlast, j0, BN);
         if (!full) {
             if (DENSE) {
@@ -662,9 +668,10 @@ fa_fwd_pp(const fa_kargs a) {
         // within the range fp32 and the 16-bit P hold; a lane sum of at most 2^16 bounds every
         // p by 2^16 (an overflow to inf, or a NaN, fails the test). Otherwise the wave takes the
         // exact path: the tile's row maximum, and the rescale when it grows by more than 2^8.
-        // An alibi bias raises the row maximum from tile to tile (the bias grows towards the
-        // diagonal), so there the fast path would mostly fail: alibi kernels take the exact one.
-        bool exact = ALIBI || __any(m_run == -INFINITY);
+        // An alibi bias rises with the key index: walked upwards (a dense mask's tile list) the
+        // row maximum would grow from tile to tile and the fast path mostly fail, so that case
+        // takes the exact path.
+        bool exact = (ALIBI && DENSE) || __any(m_run == -INFINITY);
         float lsum = 0.f;
         if (!exact) {
             lsum = expo(m_run);
@@ -767,8 +774,8 @@ fa_fwd_pp(const fa_kargs a) {
         // Page ids of this iteration's loads were fetched one iteration ago; fetch the next ones.
         const int pg_v = pg_v_next, pg_k = pg_k_next;
         if constexpr (PAGED) {
-            pg_v_next = page_of(kr.begin + t + 4);
-            pg_k_next = page_of(kr.begin + t + 5);
+            pg_v_next = page_of(kt_of(t + 4));
+            pg_k_next = page_of(kt_of(t + 5));
         }
         // Dense mask: entries of V(t + 3) and K(t + 4) were fetched one iteration ago (V(t + 4) is
         // this iteration's K), tile t + 1's two. Fetch K(t + 5) and tile t + 2.
@@ -795,8 +802,8 @@ fa_fwd_pp(const fa_kargs a) {
         fa_lds_barrier_pending<2 * NPRE>();   // the prefetched V^T reads may still be in flight
         __builtin_amdgcn_s_setprio(1);
         matmul(k_cur, v_cur, [&]() __attribute__((always_inline)) {
-            dload(vp, DENSE ? int(e_v & FA_DENSE_KT) : kr.begin + t + 3, pg_v, v_fill);
-            dload(kp, DENSE ? int(e_k & FA_DENSE_KT) : kr.begin + t + 4, pg_k, k_fill);
+            dload(vp, DENSE ? int(e_v & FA_DENSE_KT) : kt_of(t + 3), pg_v, v_fill);
+            dload(kp, DENSE ? int(e_k & FA_DENSE_KT) : kt_of(t + 4), pg_k, k_fill);
         });
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(fa_vmcnt(BATCH));
@@ -806,11 +813,11 @@ fa_fwd_pp(const fa_kargs a) {
     if (n_tiles > 0) {
         // K(0) goes into buffer 3's K half (set 3 is not loaded before iteration 0's matrix
         // phase, after both groups have used K(0)); sets 0, 1, 2 into buffers 0, 1, 2.
-        const int pg0 = page_of(kr.begin), pg1 = page_of(kr.begin + 1);
-        const int pg2 = page_of(kr.begin + 2), pg3 = page_of(kr.begin + 3);
+        const int pg0 = page_of(kt_of(0)), pg1 = page_of(kt_of(1));
+        const int pg2 = page_of(kt_of(2)), pg3 = page_of(kt_of(3));
         pg_v_next = pg3;
-        pg_k_next = page_of(kr.begin + 4);
-        int kt0 = kr.begin, kt1 = kr.begin + 1, kt2 = kr.begin + 2, kt3 = kr.begin + 3;
+        pg_k_next = page_of(kt_of(4));
+        int kt0 = kt_of(0), kt1 = kt_of(1), kt2 = kt_of(2), kt3 = kt_of(3);
         if constexpr (DENSE) {
             const uint32_t e0 = ent(0), e1 = ent(1), e2 = ent(2), e3 = ent(3);
             kt0 = int(e0 & FA_DENSE_KT);

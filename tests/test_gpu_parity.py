@@ -617,6 +617,36 @@ def test_single_key_rows_return_value(gpu_device):
     assert np.abs(lse.double().numpy() - ref).max() < 1e-4
 
 
+@pytest.mark.parametrize("mode", [0, 3])
+def test_softmax_row_max_growth(gpu_device, mode):
+    """Row maxima that move after the first tile. The kernel exponentiates each tile against
+    the row maximum it already holds and switches to the exact update (tile maximum, rescale)
+    only when a lane's sum of a tile's 32 values exceeds 2^16 or overflows. Head 0: scores
+    climb about 20 (log2 units) per 64-key tile, so every tile needs the exact update; head 1:
+    about 6 per tile, so the held maximum goes stale by more than 16 every third tile; head 2:
+    N(0, 1) scores with one key 300 above the rest (natural units) near the end of each row,
+    where the held maximum gives an infinite p."""
+    rng = np.random.default_rng(4242)
+    B, N, sq, skv, D = 1, 3, 256, 1024, 128
+    q = rng.standard_normal((B, N, sq, D)) * 0.05
+    k = rng.standard_normal((B, N, skv, D)) * 0.05
+    v = rng.standard_normal((B, N, skv, D))
+    j = np.arange(skv)
+    q[:, :2, :, 0] = 1.0
+    k[0, 0, :, 0] = 20 * np.log(2) / 64 * j
+    k[0, 1, :, 0] = 6 * np.log(2) / 64 * j
+    q[:, 2] = rng.standard_normal((sq, D)) / np.sqrt(D)
+    k[:, 2] = rng.standard_normal((skv, D)) / np.sqrt(D)
+    q[0, 2, :, 1] = 1.0
+    k[0, 2, 900, 1] = 300.0
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+    kw = dict(pre_tokens=1 << 20, next_tokens=1 << 20) if mode == 0 else {}
+    o, lse = run(q, k, v, "BNSD", mode, 1.0, gpu_device, **kw)
+    ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout="BNSD", sparse_mode=mode,
+                                   scale=1.0, **kw)
+    check(o, lse, ref_o, ref_lse, torch.bfloat16, f"row max growth mode {mode}")
+
+
 # ---------------------------------------------------------------------------------------
 # Dense mask (sparseMode=1): the pre-pass tile map and the tile-skipping kernel path
 # ---------------------------------------------------------------------------------------
