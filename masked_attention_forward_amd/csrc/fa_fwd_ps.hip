@@ -442,7 +442,6 @@ fa_fwd_ps(const fa_kargs a, const fa_ps_args ps) {
         float s[32];
 #pragma unroll
         for (int e = 0; e < 32; ++e) s[e] = sacc[e >> 4][e & 15];
-        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         if (AL == 1) {
             const float base = slope2 * float(j0 + 4 * hl - rowb);
 #pragma unroll
@@ -450,7 +449,6 @@ fa_fwd_ps(const fa_kargs a, const fa_ps_args ps) {
                 const int r = e & 15;
                 const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
                 s[e] = fmaf(s[e], sl2, fmaf(slope2, float(kc), base));
-                m4[e & 3] = fmaxf(m4[e & 3], s[e]);
             }
         } else if (AL == 2) {
             // Square-root bias: -slope sign(d) sqrt(|d|), d = i + (Skv - Sq) - j (v_sqrt_f32,
@@ -462,29 +460,45 @@ fa_fwd_ps(const fa_kargs a, const fa_ps_args ps) {
                 const int kc = 32 * (e >> 4) + 8 * (r >> 2) + (r & 3);
                 const float dd = dbase - float(kc);
                 s[e] = fmaf(s[e], sl2, -slope2 * copysignf(__builtin_amdgcn_sqrtf(fabsf(dd)), dd));
-                m4[e & 3] = fmaxf(m4[e & 3], s[e]);
             }
-        } else {
+        }
+        // p = 2^(s - m) for the maximum m in use; returns this lane's sum of the 32 values.
+        float p[32];
+        auto expo = [&](float m_use) __attribute__((always_inline)) {
+            float l4[4];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                p[e] = ALIBI ? __builtin_amdgcn_exp2f(s[e] - m_use) : __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -m_use));
+                l4[e & 3] = e < 4 ? p[e] : l4[e & 3] + p[e];
+            }
+            return (l4[0] + l4[1]) + (l4[2] + l4[3]);
+        };
+        // As in fa_fwd_pp: once the row has a maximum, exponentiate against it as it stands while
+        // every lane's sum of the tile's 32 values stays at most 2^16 (so every p does); otherwise
+        // the exact update (tile maximum; rescale when it grows by more than 2^8). This kernel
+        // walks tiles upwards, and an alibi bias then raises the maximum tile by tile: alibi
+        // kernels always take the exact update.
+        bool exact = ALIBI || __any(m_run == -INFINITY);
+        float lsum = 0.f;
+        if (!exact) {
+            lsum = expo(m_run);
+            exact = __any(!(lsum <= 65536.f));
+        }
+        float alpha = 1.f;
+        bool need = false;
+        if (exact) {
+            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
             for (int e = 0; e < 32; ++e) m4[e & 3] = fmaxf(m4[e & 3], s[e]);
+            float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+            if (!ALIBI) mx *= sl2;
+            mx = pair_max(mx);
+            need = mx > m_run + 8.f;
+            alpha = need ? exp2f(m_run - mx) : 1.f;
+            m_run = need ? mx : m_run;
+            lsum = expo(m_run == -INFINITY ? 0.f : m_run);
         }
-        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        if (!ALIBI) mx *= sl2;
-        mx = pair_max(mx);
-        // Rescale only when the row maximum grows by more than 2^8: p stays <= 256, and the
-        // final O / l and LSE do not depend on which maximum was used.
-        const bool need = mx > m_run + 8.f;
-        const float alpha = need ? exp2f(m_run - mx) : 1.f;
-        m_run = need ? mx : m_run;
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float p[32];
-        float l4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            p[e] = ALIBI ? __builtin_amdgcn_exp2f(s[e] - m_use) : __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -m_use));
-            l4[e & 3] += p[e];
-        }
-        l_run = fmaf(l_run, alpha, (l4[0] + l4[1]) + (l4[2] + l4[3]));
+        l_run = fmaf(l_run, alpha, lsum);
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
             const int base = 16 * (t4 >> 1) + 8 * (t4 & 1);
