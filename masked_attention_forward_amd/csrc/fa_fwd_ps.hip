@@ -474,7 +474,8 @@ fa_fwd_ps(const fa_kargs a, const fa_ps_args ps) {
             return (l4[0] + l4[1]) + (l4[2] + l4[3]);
         };
         // As in fa_fwd_pp: once the row has a maximum, exponentiate against it as it stands while
-        // every lane's sum of the tile's 32 values stays at most 2^16 (so every p does); otherwise
+        // every lane's sum of the tile's 32 values stays at most 2^15 (so every p does, within
+        // fp16's range); otherwise
         // the exact update (tile maximum; rescale when it grows by more than 2^8). This kernel
         // walks tiles upwards, and an alibi bias then raises the maximum tile by tile: alibi
         // kernels always take the exact update.
@@ -482,7 +483,7 @@ fa_fwd_ps(const fa_kargs a, const fa_ps_args ps) {
         float lsum = 0.f;
         if (!exact) {
             lsum = expo(m_run);
-            exact = __any(!(lsum <= 65536.f));
+            exact = __any(!(lsum <= 32768.f));
         }
         float alpha = 1.f;
         bool need = false;

@@ -665,9 +665,10 @@ fa_fwd_pp(const fa_kargs a) {
         };
         // Fast path: once the row has a maximum, exponentiate against it as it stands. The final
         // O / l and LSE do not depend on which maximum was used, only on p staying finite and
-        // within the range fp32 and the 16-bit P hold; a lane sum of at most 2^16 bounds every
-        // p by 2^16 (an overflow to inf, or a NaN, fails the test). Otherwise the wave takes the
-        // exact path: the tile's row maximum, and the rescale when it grows by more than 2^8.
+        // within the range fp32 and the 16-bit P hold; a lane sum of at most 2^15 bounds every
+        // p by 2^15, which fp16 holds (its largest finite value is 65504; an overflow to inf, or
+        // a NaN, fails the test too). Otherwise the wave takes the exact path: the tile's row
+        // maximum, and the rescale when it grows by more than 2^8.
         // An alibi bias rises with the key index: walked upwards (a dense mask's tile list) the
         // row maximum would grow from tile to tile and the fast path mostly fail, so that case
         // takes the exact path.
@@ -675,7 +676,7 @@ fa_fwd_pp(const fa_kargs a) {
         float lsum = 0.f;
         if (!exact) {
             lsum = expo(m_run);
-            exact = __any(!(lsum <= 65536.f));
+            exact = __any(!(lsum <= 32768.f));
         }
         float alpha = 1.f;
         bool need = false;

@@ -621,9 +621,9 @@ def test_single_key_rows_return_value(gpu_device):
 def test_softmax_row_max_growth(gpu_device, mode):
     """Row maxima that move after the first tile. The kernel exponentiates each tile against
     the row maximum it already holds and switches to the exact update (tile maximum, rescale)
-    only when a lane's sum of a tile's 32 values exceeds 2^16 or overflows. Head 0: scores
+    only when a lane's sum of a tile's 32 values exceeds 2^15 or overflows. Head 0: scores
     climb about 20 (log2 units) per 64-key tile, so every tile needs the exact update; head 1:
-    about 6 per tile, so the held maximum goes stale by more than 16 every third tile; head 2:
+    about 6 per tile, so the held maximum goes stale by more than 15 every third tile; head 2:
     N(0, 1) scores with one key 300 above the rest (natural units) near the end of each row,
     where the held maximum gives an infinite p."""
     rng = np.random.default_rng(4242)
@@ -645,6 +645,30 @@ def test_softmax_row_max_growth(gpu_device, mode):
     ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout="BNSD", sparse_mode=mode,
                                    scale=1.0, **kw)
     check(o, lse, ref_o, ref_lse, torch.bfloat16, f"row max growth mode {mode}")
+
+
+def test_softmax_fp16_p_range(gpu_device):
+    """fp16 inputs pack P as fp16, whose largest finite value is 65504. Keys 0..63 score 0, so the
+    held row maximum after the first tile is 0 (log2 units); key 100 then scores 11.09033203125
+    (q = e0 + e1, k = 11.0859375 e0 + 9/2048 e1, scale 1), i.e. p = 2^15.99997 = 65534 against the
+    held maximum, and every other key of the second tile scores -50 (p underflows). That lane's
+    sum stays below 2^16 with a p that rounds to inf in fp16; the kernel must take the exact update
+    for it (its bound is 2^15)."""
+    D, sq, skv = 128, 64, 128
+    q = np.zeros((1, 1, sq, D))
+    k = np.zeros((1, 1, skv, D))
+    q[..., 0] = 1.0
+    q[..., 1] = 1.0
+    k[0, 0, 64:, 0] = -50.0
+    k[0, 0, 100, 0] = 11.0859375
+    k[0, 0, 100, 1] = 9 / 2048
+    v = np.random.default_rng(77).standard_normal((1, 1, skv, D))
+    q, k, v = (torch.from_numpy(x).to(torch.float16) for x in (q, k, v))
+    kw = dict(pre_tokens=1 << 20, next_tokens=1 << 20)
+    o, lse = run(q, k, v, "BNSD", 0, 1.0, gpu_device, **kw)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout="BNSD", sparse_mode=0, scale=1.0, **kw)
+    check(o, lse, ref_o, ref_lse, torch.float16, "fp16 P range")
 
 
 # ---------------------------------------------------------------------------------------
