@@ -32,7 +32,7 @@ class FaPlanStats(ctypes.Structure):
                 ("work_items", ctypes.c_int64), ("kv_tiles_visited", ctypes.c_int64),
                 ("kv_tiles_full", ctypes.c_int64), ("kv_tiles_total", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t), ("launch_order", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("edge_skip", ctypes.c_int32)]
 
 
 class FaError(RuntimeError):

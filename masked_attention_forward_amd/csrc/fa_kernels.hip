@@ -405,7 +405,7 @@ fa_fwd_mfma(const fa_kargs a) {
 // Phase barriers order LDS only, so loads stay in flight across them.
 // ------------------------------------------------------------------------------------------
 
-template <int D, bool IS_BF16, int AL, bool DENSE, bool PAGED = false>
+template <int D, bool IS_BF16, int AL, bool DENSE, bool PAGED = false, bool EDGE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(PP_THREADS, PP_THREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 fa_fwd_pp(const fa_kargs a) {
@@ -593,6 +593,23 @@ fa_fwd_pp(const fa_kargs a) {
     f32x16 sacc[2];   // S^T of the tile waiting for its softmax
     u32x4 pop[4];     // P^T of the tile waiting for its PV product
 
+    // EDGE: true when no row of this wave sees a key of the item's tile t. The rows' intervals
+    // [lo, hi] rise with the row, so the wave's visible keys lie in [lo(first row), hi(last
+    // row)]. Such a wave skips the tile's softmax and hands a zero P^T to its PV product (its
+    // MFMAs still run: a branch around them costs the fused matrix phase its register
+    // allocation). The planner picks this variant where such tiles are a large share of the
+    // items (band edges, short causal items); the test costs long items about 0.5%.
+    const int u_row0 = i0 + wave_u * 32, u_last = min(u_row0 + 31, g.sq - 1);
+    const int w_lo = fa_row_lo(g, u_row0), w_hi = fa_row_hi(g, u_last);
+    auto wave_empty = [&](int t) __attribute__((always_inline)) {
+        if constexpr (DENSE || !EDGE) {
+            return false;
+        } else {
+            const int j0 = kt_of(t) * BN;
+            return u_row0 >= g.sq || w_hi < j0 || w_lo > j0 + BN - 1;
+        }
+    };
+
     auto qk = [&](const u32x4* kb) __attribute__((always_inline)) {
         sacc[0] = f32x16{};
         sacc[1] = f32x16{};
@@ -610,6 +627,11 @@ fa_fwd_pp(const fa_kargs a) {
     // O^T rescale happens here too: no MFMA of this wave is using the accumulators.
     // es: the dense-mask entry of tile t; hidden: its packed mask bits for this lane.
     auto softmax = [&](int t, uint32_t es, uint32_t hidden) __attribute__((always_inline)) {
+        if (wave_empty(t)) {
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) pop[t4] = u32x4{0u, 0u, 0u, 0u};
+            return;
+        }
         const int j0 = DENSE ? int(es & FA_DENSE_KT) * BN : kt_of(t) * BN;
         const bool full = DENSE ? ((es >> (24 + wave_u)) & 1u) != 0u : fa_tile_full(g, wrow0, wlast, j0, BN);
         if (!full) {
@@ -1823,10 +1845,13 @@ void launch_mfma32_d(const fa_kargs& a, int al, bool dense, dim3 grid, hipStream
 }
 
 template <int D, bool BF>
-void launch_pp_d(const fa_kargs& a, int al, bool dense, dim3 grid, hipStream_t s) {
+void launch_pp_d(const fa_kargs& a, int al, bool dense, bool edge, dim3 grid, hipStream_t s) {
     const dim3 block(PP_THREADS);
     switch (al * 2 + (dense ? 1 : 0)) {
-        case 0: fa_fwd_pp<D, BF, 0, false><<<grid, block, 0, s>>>(a); break;
+        case 0:
+            if (edge) fa_fwd_pp<D, BF, 0, false, false, true><<<grid, block, 0, s>>>(a);
+            else fa_fwd_pp<D, BF, 0, false><<<grid, block, 0, s>>>(a);
+            break;
         case 1: fa_fwd_pp<D, BF, 0, true><<<grid, block, 0, s>>>(a); break;
         case 2: fa_fwd_pp<D, BF, 1, false><<<grid, block, 0, s>>>(a); break;
         case 3: fa_fwd_pp<D, BF, 1, true><<<grid, block, 0, s>>>(a); break;
@@ -1967,11 +1992,11 @@ fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v,
     } else if (p.kernel == FA_KERNEL_PP) {
         const bool bf = dtype == FA_DTYPE_BF16;
         if (p.D == 128) {
-            if (bf) launch_pp_d<128, true>(a, alibi, dense, grid, s);
-            else launch_pp_d<128, false>(a, alibi, dense, grid, s);
+            if (bf) launch_pp_d<128, true>(a, alibi, dense, p.edge_skip, grid, s);
+            else launch_pp_d<128, false>(a, alibi, dense, p.edge_skip, grid, s);
         } else {
-            if (bf) launch_pp_d<64, true>(a, alibi, dense, grid, s);
-            else launch_pp_d<64, false>(a, alibi, dense, grid, s);
+            if (bf) launch_pp_d<64, true>(a, alibi, dense, p.edge_skip, grid, s);
+            else launch_pp_d<64, false>(a, alibi, dense, p.edge_skip, grid, s);
         }
     } else if (p.kernel == FA_KERNEL_MFMA32) {
         const bool bf = dtype == FA_DTYPE_BF16;

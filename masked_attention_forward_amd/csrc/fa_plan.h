@@ -110,6 +110,10 @@ struct fa_plan {
     size_t ws_cls_offset = 0, ws_list_offset = 0, ws_bits_offset = 0, ws_perm_offset = 0;
     // Statistics (per head).
     int64_t kv_tiles_visited = 0, kv_tiles_full = 0, kv_tiles_total = 0;
+    // Ping-pong kernel variant in which a wave skips the softmax of a kv tile none of its rows
+    // sees (band edges, causal diagonals): chosen where such tiles are a large share of the
+    // work items, see fa_make_plan.
+    bool edge_skip = false;
 };
 
 // Validates `call` against the pages' rules and this ABI; on success fills `plan`.

@@ -23,7 +23,7 @@ class Dims(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [("kernel", i32), ("block_m", i32), ("block_n", i32), ("work_items", i64),
                 ("kv_tiles_visited", i64), ("kv_tiles_full", i64), ("kv_tiles_total", i64),
-                ("workspace_bytes", sz), ("launch_order", i32), ("reserved", i32)]
+                ("workspace_bytes", sz), ("launch_order", i32), ("edge_skip", i32)]
 
 
 class Paged(ctypes.Structure):

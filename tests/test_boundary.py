@@ -602,3 +602,25 @@ def test_launch_order_choice(lib):
     tq = fb.make_dims(2, 2, B=2, N=32, D=128, T_q=3000, T_kv=3000)
     assert order(tq, "TND", 3, actual_seq_qlen=[1000, 3000], actual_seq_kvlen=[1000, 3000]) == 4
     assert order(fb.make_dims(2, 0, B=4, N=32, Sq=1, Skv=32768, D=128), "BNSD", 3) == 0
+
+
+def test_edge_skip_choice(lib):
+    """The planner's ping-pong variant with the empty-wave softmax skip (fa_plan_stats.edge_skip):
+    on for bands whose lower bound cuts some row and for items of at most 32 kv tiles; off for
+    long causal items (the headline shape), prefix modes, alibi, dense masks and decode."""
+    def edge(dims, layout, mode, **kw):
+        return fb.fa_plan_stats(dims, layout, mode, scale=0.088, **kw)["edge_skip"]
+
+    big = fb.make_dims(2, 0, B=2, N=32, Sq=8192, Skv=8192, D=128)
+    assert edge(big, "BNSD", 3) == 0
+    assert edge(fb.make_dims(2, 0, B=4, N=32, Sq=2048, Skv=2048, D=128), "BNSD", 3) == 1
+    assert edge(big, "BNSD", 4, pre_tokens=1024, next_tokens=0) == 1
+    assert edge(big, "BNSD", 0, pre_tokens=1024, next_tokens=-256) == 1
+    assert edge(big, "BNSD", 0, pre_tokens=1 << 30, next_tokens=1 << 30) == 0   # no lower bound
+    assert edge(big, "BNSD", 3, has_alibi=True) == 0
+    assert edge(big, "BNSD", 1, has_mask=True) == 0
+    assert edge(big, "BNSD", 5, prefix=[100, 2000]) == 0
+    tq = fb.make_dims(2, 2, B=2, N=32, D=128, T_q=6000, T_kv=6000)
+    assert edge(tq, "TND", 3, actual_seq_qlen=[1000, 6000], actual_seq_kvlen=[1000, 6000]) == 0
+    assert edge(fb.make_dims(2, 0, B=4, N=32, Sq=1, Skv=32768, D=128), "BNSD", 3) == 0
+    assert edge(fb.make_dims(0, 0, B=1, N=1, Sq=64, Skv=64, D=16), "BNSD", 3) == 0   # fp32: generic
