@@ -324,6 +324,8 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         bool lower = false;
         for (const fa_geom& g : p.geoms) lower = lower || int64_t(g.sq) - 1 + g.a > 0;   // some row's lo > 0
         p.edge_skip = lower || p.n_kvtiles_max <= 32;
+        if (const char* ee = std::getenv("FA_EDGE"))   // 0 | 1: override (comparisons and tests)
+            p.edge_skip = std::atoi(ee) != 0;
     }
     auto item_cost = [&](int64_t b, int64_t qt, int64_t* full) -> int64_t {
         const fa_geom& g = p.geoms[b];

@@ -796,3 +796,30 @@ def test_parity_persistent_kernel(gpu_device, monkeypatch, case):
                                        pre_tokens=2000, next_tokens=-300)
         check(o, lse, ref_o, ref_lse, torch.bfloat16, "persistent empty items")
         zero_rows_ok(o, lse, "BNSD")
+
+
+@pytest.mark.parametrize("case", ["band", "band_neg", "causal_short", "tnd_band"])
+def test_edge_variant_bitwise(gpu_device, monkeypatch, case):
+    """The EDGE variant of the ping-pong kernel (a wave that sees nothing of a kv tile skips its
+    softmax and hands a zero P^T to its PV product) must give the same bits as the plain kernel:
+    such a tile contributes p = 0 and leaves the row's max and sum alone on either path.
+    FA_EDGE forces the planner's choice; the plan stats report it."""
+    if case == "tnd_band":
+        qlens, kvlens = [300, 900, 1200], [300, 1000, 1200]
+        q, k, v = make_inputs("TND", "bf16", 3, 4, 0, 0, 128, seed=31, qlens=qlens, kvlens=kvlens)
+        kw = dict(layout="TND", mode=0, actual_seq_qlen=synth.cumulative_ends(qlens),
+                  actual_seq_kvlen=synth.cumulative_ends(kvlens), pre_tokens=300, next_tokens=0)
+    else:
+        sq = skv = 1500 if case != "causal_short" else 700
+        q, k, v = make_inputs("BNSD", "bf16", 2, 4, sq, skv, 128, seed=32)
+        kw = {"band": dict(layout="BNSD", mode=4, pre_tokens=300, next_tokens=0),
+              "band_neg": dict(layout="BNSD", mode=0, pre_tokens=400, next_tokens=-100),
+              "causal_short": dict(layout="BNSD", mode=3)}[case]
+    layout, mode = kw.pop("layout"), kw.pop("mode")
+    outs = []
+    for edge in ("0", "1"):
+        monkeypatch.setenv("FA_EDGE", edge)
+        outs.append(run(q, k, v, layout, mode, 0.088, gpu_device, **kw))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout=layout, sparse_mode=mode, scale=0.088, **kw)
+    check(outs[1][0], outs[1][1], ref_o, ref_lse, torch.bfloat16, f"edge {case}")
