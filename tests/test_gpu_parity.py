@@ -798,7 +798,7 @@ def test_parity_persistent_kernel(gpu_device, monkeypatch, case):
         zero_rows_ok(o, lse, "BNSD")
 
 
-@pytest.mark.parametrize("case", ["band", "band_neg", "causal_short", "tnd_band"])
+@pytest.mark.parametrize("case", ["band", "band_neg", "causal_short", "tnd_band", "band_f16_d64"])
 def test_edge_variant_bitwise(gpu_device, monkeypatch, case):
     """The EDGE variant of the ping-pong kernel (a wave that sees nothing of a kv tile skips its
     softmax and hands a zero P^T to its PV product) must give the same bits as the plain kernel:
@@ -811,10 +811,12 @@ def test_edge_variant_bitwise(gpu_device, monkeypatch, case):
                   actual_seq_kvlen=synth.cumulative_ends(kvlens), pre_tokens=300, next_tokens=0)
     else:
         sq = skv = 1500 if case != "causal_short" else 700
-        q, k, v = make_inputs("BNSD", "bf16", 2, 4, sq, skv, 128, seed=32)
+        dt, D = ("f16", 64) if case == "band_f16_d64" else ("bf16", 128)
+        q, k, v = make_inputs("BNSD", dt, 2, 4, sq, skv + 37 * (D == 64), D, seed=32)
         kw = {"band": dict(layout="BNSD", mode=4, pre_tokens=300, next_tokens=0),
               "band_neg": dict(layout="BNSD", mode=0, pre_tokens=400, next_tokens=-100),
-              "causal_short": dict(layout="BNSD", mode=3)}[case]
+              "causal_short": dict(layout="BNSD", mode=3),
+              "band_f16_d64": dict(layout="BNSD", mode=4, pre_tokens=200, next_tokens=5)}[case]
     layout, mode = kw.pop("layout"), kw.pop("mode")
     outs = []
     for edge in ("0", "1"):
@@ -822,4 +824,4 @@ def test_edge_variant_bitwise(gpu_device, monkeypatch, case):
         outs.append(run(q, k, v, layout, mode, 0.088, gpu_device, **kw))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     ref_o, ref_lse = ref_attention(to64(q), to64(k), to64(v), layout=layout, sparse_mode=mode, scale=0.088, **kw)
-    check(outs[1][0], outs[1][1], ref_o, ref_lse, torch.bfloat16, f"edge {case}")
+    check(outs[1][0], outs[1][1], ref_o, ref_lse, q.dtype, f"edge {case}")
