@@ -1879,10 +1879,13 @@ void launch_decode_d(const fa_kargs& a, const fa_decode_args& dc, int al, dim3 g
 }
 
 template <int D, bool BF>
-void launch_pp_paged_d(const fa_kargs& a, int al, dim3 grid, hipStream_t s) {
+void launch_pp_paged_d(const fa_kargs& a, int al, bool edge, dim3 grid, hipStream_t s) {
     const dim3 block(PP_THREADS);
     switch (al) {
-        case 0: fa_fwd_pp<D, BF, 0, false, true><<<grid, block, 0, s>>>(a); break;
+        case 0:
+            if (edge) fa_fwd_pp<D, BF, 0, false, true, true><<<grid, block, 0, s>>>(a);
+            else fa_fwd_pp<D, BF, 0, false, true><<<grid, block, 0, s>>>(a);
+            break;
         case 1: fa_fwd_pp<D, BF, 1, false, true><<<grid, block, 0, s>>>(a); break;
         default: fa_fwd_pp<D, BF, 2, false, true><<<grid, block, 0, s>>>(a); break;
     }
@@ -1975,11 +1978,11 @@ fa_status run_fwd(const fa_call& c, const void* q, const void* k, const void* v,
     } else if (p.kernel == FA_KERNEL_PP && p.paged) {
         const bool bf = dtype == FA_DTYPE_BF16;
         if (p.D == 128) {
-            if (bf) launch_pp_paged_d<128, true>(a, alibi, grid, s);
-            else launch_pp_paged_d<128, false>(a, alibi, grid, s);
+            if (bf) launch_pp_paged_d<128, true>(a, alibi, p.edge_skip, grid, s);
+            else launch_pp_paged_d<128, false>(a, alibi, p.edge_skip, grid, s);
         } else {
-            if (bf) launch_pp_paged_d<64, true>(a, alibi, grid, s);
-            else launch_pp_paged_d<64, false>(a, alibi, grid, s);
+            if (bf) launch_pp_paged_d<64, true>(a, alibi, p.edge_skip, grid, s);
+            else launch_pp_paged_d<64, false>(a, alibi, p.edge_skip, grid, s);
         }
     } else if (p.kernel == FA_KERNEL_PP && !dense && persist_enabled() && [&] {
                    fa_ps_args ps;

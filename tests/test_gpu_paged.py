@@ -266,3 +266,29 @@ def test_paged_full_size_matches_dense(gpu_device, cache_layout):
     o2, lse2 = fb.flash_attention(qd, kd, vd, layout=w.layout, sparse_mode=w.sparse_mode, scale=w.softmax_scale)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("case", ["band", "causal_short"])
+def test_paged_edge_variant_bitwise(gpu_device, monkeypatch, case):
+    """The paged ping-pong kernel's EDGE variant (a wave that sees nothing of a kv tile skips its
+    softmax) gives the same bits as the plain paged kernel and as the dense forward on the same
+    K / V, read from 128-key pages in a random order. FA_EDGE forces the planner's choice."""
+    B, N, S, D, bs = 2, 4, 1500 if case == "band" else 700, 128, 128
+    q, k, v = make_inputs("BSND", "bf16", B, N, S, S, D, seed=4321)
+    rng = np.random.default_rng(4321)
+    nb = B * (-(-S // bs)) + 5
+    bt = make_table([S] * B, nb, bs, rng)
+    dev = gpu_device
+    kc = fill_cache(seqs_of(k, "BSND"), bt, nb, bs, "Norm", torch.bfloat16, dev, seed=1)
+    vc = fill_cache(seqs_of(v, "BSND"), bt, nb, bs, "Norm", torch.bfloat16, dev, seed=2)
+    kw = dict(sparse_mode=4, pre_tokens=300, next_tokens=0) if case == "band" else dict(sparse_mode=3)
+    print(f"[case] paged edge {case} S={S}", flush=True)
+    outs = []
+    for edge in ("0", "1"):
+        monkeypatch.setenv("FA_EDGE", edge)
+        outs.append(fb.paged_attention(q.to(dev), kc, vc, torch.from_numpy(bt).to(dev), layout="BSND",
+                                       cache_layout="Norm", kv_seqlen=S, scale=0.0884, **kw))
+    dense = fb.flash_attention(q.to(dev), k.to(dev), v.to(dev), layout="BSND", scale=0.0884, **kw)
+    torch.cuda.synchronize()
+    for o, lse in outs[1:] + [dense]:
+        assert torch.equal(outs[0][0], o) and torch.equal(outs[0][1], lse)
