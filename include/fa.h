@@ -242,7 +242,7 @@ typedef struct fa_plan_stats {
                                   0 for the split-KV decode kernel */
     int32_t edge_skip;         /* 1: the ping-pong kernel's variant in which a wave skips the
                                   softmax of a kv tile none of its rows sees (chosen for bands
-                                  with a lower bound and for items of at most 32 kv tiles) */
+                                  with a lower bound and for items of at most 64 kv tiles) */
 } fa_plan_stats;
 
 fa_status fa_plan_stats_get(const fa_dims* dims, int32_t layout, int32_t sparse_mode,

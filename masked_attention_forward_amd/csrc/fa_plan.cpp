@@ -317,13 +317,13 @@ static fa_status make_plan_impl(const fa_call& call, bool with_tables, bool size
         p.n_kvtiles_max = std::max(p.n_kvtiles_max, ceil_div(skv[b], p.bn));
     }
     // The skip costs a uniform test per tile, which measured about 0.5% on long causal items
-    // (2 x 32 x 8192^2) and gained 2-5% where edge tiles are a large share of each item: a band
-    // with a lower bound (modes 0 and 4, the band batch of 7 / 8) or items of at most 32 kv
-    // tiles. Dense masks and alibi keep the plain kernel.
+    // (2 x 32 x 8192^2, 128-tile items) and gained 1-8% where edge tiles are a larger share of
+    // each item: a band with a lower bound (modes 0 and 4, the band batch of 7 / 8) or items of
+    // at most 64 kv tiles (varlen with sequences up to 4096 keys: +1.2%). Dense masks and alibi keep the plain kernel.
     if (p.kernel == FA_KERNEL_PP && mode != 1 && !call.has_alibi) {
         bool lower = false;
         for (const fa_geom& g : p.geoms) lower = lower || int64_t(g.sq) - 1 + g.a > 0;   // some row's lo > 0
-        p.edge_skip = lower || p.n_kvtiles_max <= 32;
+        p.edge_skip = lower || p.n_kvtiles_max <= 64;
         if (const char* ee = std::getenv("FA_EDGE"))   // 0 | 1: override (comparisons and tests)
             p.edge_skip = std::atoi(ee) != 0;
     }

@@ -606,7 +606,7 @@ def test_launch_order_choice(lib):
 
 def test_edge_skip_choice(lib):
     """The planner's ping-pong variant with the empty-wave softmax skip (fa_plan_stats.edge_skip):
-    on for bands whose lower bound cuts some row and for items of at most 32 kv tiles; off for
+    on for bands whose lower bound cuts some row and for items of at most 64 kv tiles; off for
     long causal items (the headline shape), prefix modes, alibi, dense masks and decode."""
     def edge(dims, layout, mode, **kw):
         return fb.fa_plan_stats(dims, layout, mode, scale=0.088, **kw)["edge_skip"]
@@ -622,5 +622,8 @@ def test_edge_skip_choice(lib):
     assert edge(big, "BNSD", 5, prefix=[100, 2000]) == 0
     tq = fb.make_dims(2, 2, B=2, N=32, D=128, T_q=6000, T_kv=6000)
     assert edge(tq, "TND", 3, actual_seq_qlen=[1000, 6000], actual_seq_kvlen=[1000, 6000]) == 0
+    t4 = fb.make_dims(2, 2, B=2, N=32, D=128, T_q=5096, T_kv=5096)
+    assert edge(t4, "TND", 3, actual_seq_qlen=[1000, 5096], actual_seq_kvlen=[1000, 5096]) == 1
+    assert edge(fb.make_dims(2, 0, B=2, N=32, Sq=4097, Skv=4097, D=128), "BNSD", 3) == 0
     assert edge(fb.make_dims(2, 0, B=4, N=32, Sq=1, Skv=32768, D=128), "BNSD", 3) == 0
     assert edge(fb.make_dims(0, 0, B=1, N=1, Sq=64, Skv=64, D=16), "BNSD", 3) == 0   # fp32: generic
